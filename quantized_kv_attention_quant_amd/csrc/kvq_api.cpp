@@ -1,0 +1,291 @@
+// C ABI of libkvq (declared in include/kvq.h): argument validation, cache
+// bookkeeping, launch planning.  Every check runs before the first HIP call,
+// so a rejected call enqueues nothing and leaves the struct untouched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kvq_internal.h"
+
+#define KVQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using kvq::cdiv;
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr int kWavesPerGroup = 4;      // attention workgroup = 4 waves
+constexpr int kTargetGroups = 512;     // ~2 workgroups per CU on 256 CUs
+constexpr int kTopkChunk = 1024;       // tokens per top-k workgroup
+constexpr int kMaxTopk = 256;
+
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Shape rules of kv_cache_layout; returns KVQ_OK or an error with message.
+int check_shape(const kvq_cache* c) {
+  if (!c) return fail(KVQ_EINVAL, "cache is NULL");
+  if (c->B < 1 || c->Hkv < 1) return fail(KVQ_EINVAL, "B and Hkv must be >= 1");
+  if (c->d != 64 && c->d != 128) return fail(KVQ_EINVAL, "d must be 64 or 128");
+  if (c->bits != 8 && c->bits != 2 && c->bits != 1)
+    return fail(KVQ_EINVAL, "bits must be 8, 2 or 1");
+  if (c->bits == 1 && c->d != 128)
+    return fail(KVQ_EINVAL, "1-bit codes need d == 128");
+  if (c->G < 32 || c->G % 32) return fail(KVQ_EINVAL, "G must be a multiple of 32");
+  if (c->L_max < c->G || c->L_max % c->G)
+    return fail(KVQ_EINVAL, "L_max must be a positive multiple of G");
+  if (c->Gv < 16 || c->Gv % 16 || c->d % c->Gv || c->d / c->Gv > 4)
+    return fail(KVQ_EINVAL,
+                "Gv must be a multiple of 16 dividing d with d/Gv <= 4");
+  if (c->R < c->G) return fail(KVQ_EINVAL, "R must be >= G");
+  if (c->max_append < 1) return fail(KVQ_EINVAL, "max_append must be >= 1");
+  return KVQ_OK;
+}
+
+// A cache handed to a work call must have gone through kv_cache_layout and
+// have every buffer set.
+int check_cache(const kvq_cache* c) {
+  int rc = check_shape(c);
+  if (rc) return rc;
+  if (c->ring != round_up((int64_t)c->R + c->max_append, 32))
+    return fail(KVQ_EINVAL, "cache not laid out (call kv_cache_layout)");
+  if (c->n_q < 0 || c->n_r < 0 || c->n_q % c->G || c->n_q > c->L_max ||
+      c->n_r > c->ring)
+    return fail(KVQ_EINVAL, "cache counters are inconsistent");
+  if (!c->k_hi || !c->v_hi || !c->k_sz || !c->v_sz || !c->k_res || !c->v_res)
+    return fail(KVQ_EINVAL, "a cache buffer pointer is NULL");
+  if ((c->bits == 8) != (c->k_lo != nullptr) ||
+      (c->bits == 8) != (c->v_lo != nullptr))
+    return fail(KVQ_EINVAL, "k_lo/v_lo must be set exactly when bits == 8");
+  return KVQ_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(KVQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- attention split plan --------------------------------------------------
+struct Plan {
+  int rows, rows_pad, tpw, s_q, s_r, s_alloc;
+};
+
+int s_target(const kvq_cache* c) {
+  const int64_t blocks = (int64_t)c->B * c->Hkv;
+  int64_t t = cdiv(kTargetGroups, blocks);
+  const int64_t cap = 2LL * c->d - cdiv(cdiv(c->ring, 32), kWavesPerGroup);
+  if (t > cap) t = cap;
+  return t < 1 ? 1 : (int)t;
+}
+
+int s_alloc_of(const kvq_cache* c) {
+  return s_target(c) + (int)cdiv(cdiv(c->ring, 32), kWavesPerGroup);
+}
+
+Plan plan_attn(const kvq_cache* c, int T, int Hq) {
+  Plan p;
+  const int gs = Hq / c->Hkv;
+  p.rows = T * gs;
+  p.rows_pad = p.rows <= 16 ? 16 : 32;
+  const int64_t nqt = c->n_q / 32;
+  const int st = s_target(c);
+  p.tpw = (int)(nqt <= (int64_t)kWavesPerGroup * st
+                    ? 1
+                    : cdiv(nqt, (int64_t)kWavesPerGroup * st));
+  p.s_q = (int)cdiv(nqt, (int64_t)kWavesPerGroup * p.tpw);
+  p.s_r = (int)cdiv(cdiv(c->n_r, 32), kWavesPerGroup);
+  p.s_alloc = s_alloc_of(c);
+  return p;
+}
+
+size_t ticket_bytes(const kvq_cache* c) {
+  return (size_t)round_up((int64_t)c->B * c->Hkv * 4, 256);
+}
+
+}  // namespace
+
+KVQ_API int kv_cache_layout(kvq_cache* c) {
+  int rc = check_shape(c);
+  if (rc) return rc;
+  const int64_t blocks = (int64_t)c->B * c->Hkv;
+  const int w = kvq::plane_width(c->bits);
+  const int64_t ring = round_up((int64_t)c->R + c->max_append, 32);
+  if (ring > (1 << 30)) return fail(KVQ_EINVAL, "R + max_append too large");
+  c->ring = (int32_t)ring;
+  c->bytes_k_plane = blocks * c->L_max * c->d * w / 8;
+  c->bytes_v_plane = c->bytes_k_plane;
+  c->bytes_k_sz = blocks * (c->L_max / c->G) * c->d * 4;
+  c->bytes_v_sz = blocks * c->L_max * (c->d / c->Gv) * 4;
+  c->bytes_k_res = blocks * ring * c->d * 2;
+  c->bytes_v_res = c->bytes_k_res;
+  c->n_q = 0;
+  c->n_r = 0;
+  return KVQ_OK;
+}
+
+KVQ_API int kv_quant_append(kvq_cache* c, const void* k_new, const void* v_new,
+                            int n, void* stream) {
+  int rc = check_cache(c);
+  if (rc) return rc;
+  if (!k_new || !v_new) return fail(KVQ_EINVAL, "k_new/v_new is NULL");
+  if (n < 1) return fail(KVQ_EINVAL, "n must be >= 1");
+  const int64_t total = c->n_r + (int64_t)n;
+  const int64_t f = total > c->R ? cdiv(total - c->R, c->G) : 0;
+  if (c->n_q + f * c->G > c->L_max)
+    return fail(KVQ_ECAPACITY, "append of %d tokens needs %lld quantized slots, "
+                "L_max is %d", n, (long long)(c->n_q + f * c->G), c->L_max);
+  if (f * c->G / 32 > INT32_MAX)
+    return fail(KVQ_EUNSUPPORTED, "append too large for one call");
+
+  kvq::AppendArgs a;
+  a.g = kvq::geom_of(c);
+  a.p = kvq::ptrs_of(c);
+  a.k_new = (const __half*)k_new;
+  a.v_new = (const __half*)v_new;
+  a.n = n;
+  a.q0 = c->n_q;
+  a.new0 = c->n_q + c->n_r;
+  a.groups = (int)f;
+  const int64_t keep0 = c->n_q + f * c->G;          // first surviving position
+  a.wr_first = (int)(keep0 > a.new0 ? keep0 - a.new0 : 0);
+  a.wr_count = n - a.wr_first;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (total <= c->ring) {
+    e = kvq::launch_append(a, true, true, s);
+  } else {
+    e = kvq::launch_append(a, true, false, s);
+    if (e == hipSuccess) e = kvq::launch_append(a, false, true, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "kv_quant_append launch");
+  c->n_q += f * c->G;
+  c->n_r = total - f * c->G;
+  return KVQ_OK;
+}
+
+KVQ_API int kv_rollback(kvq_cache* c, int m) {
+  if (!c) return fail(KVQ_EINVAL, "cache is NULL");
+  if (m < 0) return fail(KVQ_EINVAL, "m must be >= 0");
+  if (m > c->n_r)
+    return fail(KVQ_EROLLBACK, "rollback of %d tokens, residual holds %lld", m,
+                (long long)c->n_r);
+  c->n_r -= m;
+  return KVQ_OK;
+}
+
+KVQ_API size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq) {
+  if (check_shape(c) || T < 1 || Hq < 1 || Hq % c->Hkv) return 0;
+  const int rows = T * (Hq / c->Hkv);
+  const int rows_pad = rows <= 16 ? 16 : 32;
+  return ticket_bytes(c) + (size_t)c->B * c->Hkv * s_alloc_of(c) * rows_pad *
+                               (c->d + 2) * sizeof(float);
+}
+
+KVQ_API int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq,
+                           int path, float sm_scale, void* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_cache(c);
+  if (rc) return rc;
+  if (!q || !out) return fail(KVQ_EINVAL, "q/out is NULL");
+  if (T < 1 || T > 16) return fail(KVQ_EINVAL, "T must be in [1, 16]");
+  if (T > c->n_r)
+    return fail(KVQ_EINVAL, "T = %d exceeds the %lld residual tokens", T,
+                (long long)c->n_r);
+  if (Hq < 1 || Hq % c->Hkv) return fail(KVQ_EINVAL, "Hq must be a multiple of Hkv");
+  if (T * (Hq / c->Hkv) > 32)
+    return fail(KVQ_EUNSUPPORTED, "T * Hq/Hkv = %d rows exceeds 32",
+                T * (Hq / c->Hkv));
+  if (path != KVQ_TARGET && path != KVQ_DRAFT4)
+    return fail(KVQ_EINVAL, "unknown path %d", path);
+  if (path == KVQ_DRAFT4 && c->bits != 8)
+    return fail(KVQ_EINVAL, "the draft path reads 8-bit caches only");
+  if (!std::isfinite(sm_scale)) return fail(KVQ_EINVAL, "sm_scale not finite");
+  const size_t need = kv_attn_workspace_bytes(c, T, Hq);
+  if (!ws || ws_bytes < need)
+    return fail(KVQ_EWORKSPACE, "workspace needs %zu bytes", need);
+
+  const Plan p = plan_attn(c, T, Hq);
+  kvq::AttnArgs a;
+  a.g = kvq::geom_of(c);
+  a.p = kvq::ptrs_of(c);
+  a.q = (const __half*)q;
+  a.out = (__half*)out;
+  a.lse = lse;
+  a.tickets = (unsigned*)ws;
+  a.ws = (float*)((char*)ws + ticket_bytes(c));
+  a.n_q = c->n_q;
+  a.n_r = c->n_r;
+  a.T = T;
+  a.Hq = Hq;
+  a.gs = Hq / c->Hkv;
+  a.rows = p.rows;
+  a.path = path;
+  a.c0 = sm_scale * 1.4426950408889634f;
+  a.waves = kWavesPerGroup;
+  a.tpw = p.tpw;
+  a.s_q = p.s_q;
+  a.s_r = p.s_r;
+  a.s_alloc = p.s_alloc;
+  a.rows_pad = p.rows_pad;
+  hipError_t e = kvq::launch_attn(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_attn_verify launch");
+  return KVQ_OK;
+}
+
+KVQ_API size_t kv_topk_workspace_bytes(const kvq_cache* c, int Hq, int k) {
+  if (check_shape(c) || Hq < 1 || k < 1) return 0;
+  const int64_t chunks = cdiv(c->L_max, kTopkChunk);
+  return ticket_bytes(c) +
+         (size_t)c->B * c->Hkv * chunks * k * sizeof(unsigned long long);
+}
+
+KVQ_API int kv_topk(const kvq_cache* c, const void* q_spec, int Hq, int path,
+                    int k, int32_t* idx, float* key, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_cache(c);
+  if (rc) return rc;
+  if (!q_spec || !idx) return fail(KVQ_EINVAL, "q_spec/idx is NULL");
+  if (k < 1 || k > kMaxTopk) return fail(KVQ_EINVAL, "k must be in [1, 256]");
+  if (Hq < 1 || Hq % c->Hkv) return fail(KVQ_EINVAL, "Hq must be a multiple of Hkv");
+  const int gs = Hq / c->Hkv;
+  if (gs != 1 && gs != 2 && gs != 4 && gs != 8)
+    return fail(KVQ_EUNSUPPORTED, "Hq/Hkv must be 1, 2, 4 or 8");
+  if (path != KVQ_TARGET && path != KVQ_DRAFT4)
+    return fail(KVQ_EINVAL, "unknown path %d", path);
+  if (path == KVQ_DRAFT4 && c->bits != 8)
+    return fail(KVQ_EINVAL, "the draft path reads 8-bit caches only");
+  const size_t need = kv_topk_workspace_bytes(c, Hq, k);
+  if (!ws || ws_bytes < need)
+    return fail(KVQ_EWORKSPACE, "workspace needs %zu bytes", need);
+
+  kvq::TopkArgs a;
+  a.g = kvq::geom_of(c);
+  a.p = kvq::ptrs_of(c);
+  a.q = (const __half*)q_spec;
+  a.idx = idx;
+  a.key = key;
+  a.tickets = (unsigned*)ws;
+  a.cand = (unsigned long long*)((char*)ws + ticket_bytes(c));
+  a.n_q = c->n_q;
+  a.Hq = Hq;
+  a.gs = gs;
+  a.k = k;
+  a.path = path;
+  a.chunk = kTopkChunk;
+  a.chunks = (int)(c->n_q > 0 ? cdiv(c->n_q, kTopkChunk) : 1);
+  hipError_t e = kvq::launch_topk(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_topk launch");
+  return KVQ_OK;
+}
+
+KVQ_API const char* kv_last_error(void) { return g_err.c_str(); }

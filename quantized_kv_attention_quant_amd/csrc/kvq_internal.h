@@ -1,0 +1,136 @@
+// Internal definitions shared by the libkvq HIP sources (not part of the
+// public ABI).  Layouts and arithmetic are those documented in kvq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kTile = 32;       // tokens per V tile / ring tile
+constexpr int kWave = 64;       // CDNA wavefront width
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) {
+  return (a + b - 1) / b;
+}
+
+// Bits per code in one stored plane: 8-bit codes live in two nibble planes.
+__host__ __device__ inline int plane_width(int bits) {
+  return bits == 8 ? 4 : bits;
+}
+
+// Geometry of one cache, flattened for kernels (all strides in elements of
+// the buffer's own type).
+struct CacheGeom {
+  int B, Hkv, d, G, Gv, bits, R, ring;
+  int64_t L_max;
+  int w;                      // plane width in bits
+  int64_t k_row_bytes;        // d*w/8
+  int64_t k_block_bytes;      // L_max * k_row_bytes
+  int64_t v_tile_bytes;       // 4*d*w
+  int64_t v_block_bytes;      // (L_max/32) * v_tile_bytes
+  int64_t ksz_block;          // half2 per block in k_sz: (L_max/G)*d
+  int64_t vsz_tile;           // half2 per tile in v_sz: 32*(d/Gv)
+  int64_t vsz_block;          // (L_max/32)*vsz_tile
+  int64_t res_block;          // halfs per block in k_res / v_res: ring*d
+};
+
+inline CacheGeom geom_of(const kvq_cache* c) {
+  CacheGeom g;
+  g.B = c->B; g.Hkv = c->Hkv; g.d = c->d; g.G = c->G; g.Gv = c->Gv;
+  g.bits = c->bits; g.R = c->R; g.ring = c->ring; g.L_max = c->L_max;
+  g.w = plane_width(c->bits);
+  g.k_row_bytes = (int64_t)c->d * g.w / 8;
+  g.k_block_bytes = g.L_max * g.k_row_bytes;
+  g.v_tile_bytes = 4LL * c->d * g.w;
+  g.v_block_bytes = (g.L_max / kTile) * g.v_tile_bytes;
+  g.ksz_block = (g.L_max / c->G) * c->d;
+  g.vsz_tile = (int64_t)kTile * (c->d / c->Gv);
+  g.vsz_block = (g.L_max / kTile) * g.vsz_tile;
+  g.res_block = (int64_t)c->ring * c->d;
+  return g;
+}
+
+// Raw device pointers of a cache.
+struct CachePtrs {
+  uint8_t *k_hi, *k_lo, *v_hi, *v_lo;
+  __half2 *k_sz, *v_sz;
+  __half *k_res, *v_res;
+};
+
+inline CachePtrs ptrs_of(const kvq_cache* c) {
+  CachePtrs p;
+  p.k_hi = (uint8_t*)c->k_hi; p.k_lo = (uint8_t*)c->k_lo;
+  p.v_hi = (uint8_t*)c->v_hi; p.v_lo = (uint8_t*)c->v_lo;
+  p.k_sz = (__half2*)c->k_sz; p.v_sz = (__half2*)c->v_sz;
+  p.k_res = (__half*)c->k_res; p.v_res = (__half*)c->v_res;
+  return p;
+}
+
+// Half index of (slot j in a 32-slot ring tile, channel c) in v_res.
+__host__ __device__ inline int vres_index(int j, int c, int d) {
+  int g = (j & 15) >> 2, i = j & 3, h = j >> 4, r = c & 15, m = c >> 4;
+  return (16 * g + r) * (d / 2) + 8 * m + 2 * i + h;
+}
+
+// ---- launchers (defined in the .hip files; return hipError_t) ----------
+
+// Append/flush: see kv_quant_append.  Items [flush_begin, flush_end) are
+// groups of G tokens to quantize starting at absolute position q0; ring
+// items write tokens [wr_begin, wr_end) of k_new/v_new to the ring.
+struct AppendArgs {
+  CacheGeom g;
+  CachePtrs p;
+  const __half* k_new;
+  const __half* v_new;
+  int n;            // tokens in k_new/v_new
+  int64_t q0;       // first position to quantize (= n_q before the call)
+  int64_t new0;     // absolute position of k_new[0] (= n_q + n_r before)
+  int groups;       // K groups to flush (each G tokens)
+  int wr_first;     // first k_new index that goes to the ring
+  int wr_count;     // how many k_new tokens go to the ring
+};
+hipError_t launch_append(const AppendArgs& a, bool flush, bool ring_write,
+                         hipStream_t s);
+
+struct AttnArgs {
+  CacheGeom g;
+  CachePtrs p;
+  const __half* q;
+  __half* out;
+  float* lse;
+  float* ws;        // partials workspace (after the ticket area)
+  unsigned* tickets;
+  int64_t n_q, n_r;
+  int T, Hq, gs, rows;
+  int path;         // KVQ_TARGET / KVQ_DRAFT4
+  float c0;         // sm_scale * log2(e)
+  // split plan
+  int waves;        // waves per workgroup
+  int tpw;          // quantized tiles per wave
+  int s_q;          // quantized-split workgroups per block
+  int s_r;          // residual workgroups per block
+  int s_alloc;      // partial slots per block in the workspace
+  int rows_pad;     // 16 * row tiles
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+struct TopkArgs {
+  CacheGeom g;
+  CachePtrs p;
+  const __half* q;   // [B][Hq][d]
+  int32_t* idx;
+  float* key;
+  unsigned long long* cand;  // [B*Hkv][chunks][k]
+  unsigned* tickets;
+  int64_t n_q;
+  int Hq, gs, k, path;
+  int chunk;         // tokens per workgroup
+  int chunks;        // workgroups per block
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,187 @@
+"""CPU tests of the C ABI: the built library exports every function the
+header declares, the ctypes struct matches the C layout, and every argument
+error is reported before any HIP call (no GPU is touched here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_kv_attention_quant_amd as kq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+pytestmark = pytest.mark.skipif(
+    not os.path.exists(kq.LIB_PATH),
+    reason="libkvq.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(kv_\w+)\(",
+                          text, re.M))
+
+
+def test_exports_match_header():
+    names = _declared()
+    assert names == {"kv_cache_layout", "kv_quant_append", "kv_rollback",
+                     "kv_attn_workspace_bytes", "kv_attn_verify",
+                     "kv_topk_workspace_bytes", "kv_topk", "kv_last_error"}
+    out = subprocess.run(["nm", "-D", "--defined-only", kq.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert names <= exported
+    L = kq.lib()
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_struct_layout_matches_c(tmp_path):
+    fields = [f for f, _ in kq.KvqCacheStruct._fields_]
+    src = tmp_path / "probe.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "kvq.h"\n'
+        "int main(void){printf(\"%zu\\n\", sizeof(kvq_cache));\n"
+        + "".join(f'printf("%zu\\n", offsetof(kvq_cache, {f}));\n'
+                  for f in fields) + "return 0;}\n")
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True,
+                                           text=True, check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(kq.KvqCacheStruct)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(kq.KvqCacheStruct, f).offset == off, f
+
+
+def _shape(**kw):
+    c = kq.KvqCacheStruct()
+    base = dict(B=1, Hkv=8, d=128, G=128, Gv=64, bits=8, R=256, L_max=32768,
+                max_append=32)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_layout_sizes():
+    c = _shape()
+    kq.kv_cache_layout(c)
+    assert c.ring == 288
+    assert c.bytes_k_plane == 8 * 32768 * 64
+    assert c.bytes_k_sz == 8 * 256 * 128 * 4
+    assert c.bytes_v_sz == 8 * 32768 * 2 * 4
+    assert c.bytes_k_res == 8 * 288 * 128 * 2
+    c1 = _shape(bits=1, G=32, Gv=32, R=32, B=36)
+    kq.kv_cache_layout(c1)
+    assert c1.bytes_k_plane == 36 * 8 * 32768 * 16
+    assert c1.ring == 64
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(bits=4), dict(bits=1, d=64),
+                                dict(G=48), dict(L_max=1000), dict(Gv=24),
+                                dict(Gv=16), dict(R=64), dict(max_append=0),
+                                dict(B=0)])
+def test_layout_rejects(kw):
+    c = _shape(**kw)
+    with pytest.raises(kq.KvqError) as e:
+        kq.kv_cache_layout(c)
+    assert e.value.code == kq.KVQ_EINVAL
+    assert kq.kv_last_error()
+
+
+def _fake_cache(bits=8, n_q=0, n_r=0, **kw):
+    """A laid-out cache whose buffer pointers are non-NULL placeholders.
+    Only used for calls that must fail validation, so nothing is
+    dereferenced and no HIP call is made."""
+    c = _shape(bits=bits, **kw)
+    kq.kv_cache_layout(c)
+    for name in ("k_hi", "v_hi", "k_sz", "v_sz", "k_res", "v_res"):
+        setattr(c, name, 0x1000)
+    if bits == 8:
+        c.k_lo = c.v_lo = 0x1000
+    c.n_q, c.n_r = n_q, n_r
+    return c
+
+
+class FakeT:
+    def __init__(self, n=0):
+        self.n = n
+
+    def data_ptr(self):
+        return 0x2000
+
+    def numel(self):
+        return self.n
+
+
+def _code(fn):
+    with pytest.raises(kq.KvqError) as e:
+        fn()
+    return e.value.code
+
+
+def test_rollback_errors_and_update():
+    c = _fake_cache(n_q=256, n_r=40)
+    kq.kv_rollback(c, 5)
+    assert c.n_r == 35 and c.n_q == 256
+    assert _code(lambda: kq.kv_rollback(c, 36)) == kq.KVQ_EROLLBACK
+    assert _code(lambda: kq.kv_rollback(c, -1)) == kq.KVQ_EINVAL
+    assert c.n_r == 35
+
+
+def test_append_errors_before_launch():
+    c = _fake_cache(n_q=32768, n_r=250)
+    # 250 + 10 > R: one more group would pass L_max
+    assert _code(lambda: kq.kv_quant_append(c, FakeT(), FakeT(), 10, 0)) \
+        == kq.KVQ_ECAPACITY
+    assert (c.n_q, c.n_r) == (32768, 250)
+    assert _code(lambda: kq.kv_quant_append(c, None, FakeT(), 1, 0)) \
+        == kq.KVQ_EINVAL
+    assert _code(lambda: kq.kv_quant_append(c, FakeT(), FakeT(), 0, 0)) \
+        == kq.KVQ_EINVAL
+    c2 = _fake_cache()
+    c2.k_lo = None
+    assert _code(lambda: kq.kv_quant_append(c2, FakeT(), FakeT(), 1, 0)) \
+        == kq.KVQ_EINVAL
+
+
+def test_verify_errors_before_launch():
+    c = _fake_cache(n_q=1024, n_r=40)
+    ws = FakeT(kq.kv_attn_workspace_bytes(c, 7, 32))
+    assert ws.n > 0
+    call = lambda T=7, Hq=32, path=0, ws=ws, c=c: kq.kv_attn_verify(
+        c, FakeT(), T, Hq, path, 0.088, FakeT(), None, ws, 0)
+    assert _code(lambda: call(T=0)) == kq.KVQ_EINVAL
+    assert _code(lambda: call(T=17)) == kq.KVQ_EINVAL
+    assert _code(lambda: call(T=9, Hq=32)) == kq.KVQ_EUNSUPPORTED  # 36 rows
+    assert _code(lambda: call(Hq=30)) == kq.KVQ_EINVAL
+    assert _code(lambda: call(path=5)) == kq.KVQ_EINVAL
+    assert _code(lambda: call(ws=FakeT(ws.n - 1))) == kq.KVQ_EWORKSPACE
+    assert _code(lambda: call(ws=None)) == kq.KVQ_EWORKSPACE
+    short = _fake_cache(n_q=1024, n_r=3)
+    assert _code(lambda: call(c=short)) == kq.KVQ_EINVAL    # T > n_r
+    low = _fake_cache(bits=2, G=32, Gv=32, R=32, n_q=1024, n_r=8)
+    assert _code(lambda: call(c=low, path=kq.KVQ_DRAFT4)) == kq.KVQ_EINVAL
+
+
+def test_topk_errors_before_launch():
+    c = _fake_cache(n_q=1024, n_r=40)
+    ws = FakeT(kq.kv_topk_workspace_bytes(c, 32, 64))
+    call = lambda k=64, Hq=32, ws=ws, c=c, path=0: kq.kv_topk(
+        c, FakeT(), Hq, path, k, FakeT(), None, ws, 0)
+    assert _code(lambda: call(k=0)) == kq.KVQ_EINVAL
+    assert _code(lambda: call(k=257)) == kq.KVQ_EINVAL
+    assert _code(lambda: call(Hq=24)) == kq.KVQ_EUNSUPPORTED     # gs = 3
+    assert _code(lambda: call(ws=FakeT(8))) == kq.KVQ_EWORKSPACE
+    low = _fake_cache(bits=1, G=32, Gv=32, R=32, n_q=1024, n_r=8)
+    assert _code(lambda: call(c=low, path=kq.KVQ_DRAFT4)) == kq.KVQ_EINVAL
+
+
+def test_uninitialised_cache_rejected():
+    c = _shape()
+    c.k_hi = 0x1000
+    assert _code(lambda: kq.kv_quant_append(c, FakeT(), FakeT(), 1, 0)) \
+        == kq.KVQ_EINVAL
