@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark: speculative verify step over a 32K-context quantized KV cache.
+
+Workload (one GPU): a Llama-3-8B-shaped GQA attention layer, B=1, Hq=32,
+Hkv=8, d=128, context 32768, key groups G=128, value groups of 64 channels,
+fp16 residual of R=256 tokens, INT8 codes in two nibble planes.  Synthetic
+seeded K/V (N(0,1), 4 outlier key channels x10, per-token lognormal(0,0.5)
+key drift), random queries.
+
+One step = one pass of the hot path for a gamma = 6 speculative step:
+  kv_quant_append  of the 7 new tokens (fp16 ring write; no flush is due)
+  kv_attn_verify   INT4 draft attention, T=1 (upper nibble plane only)
+  kv_attn_verify   INT8 target verify attention, T=7 (causal among the 7)
+  kv_rollback      of the 7 tokens (host counters; the next step reuses them)
+Each step works on a different copy of the layer's cache (8 copies, 0.57 GB)
+so that, as in a model with many layers, a step never finds its cache in the
+256 MB Infinity Cache.
+
+The JSON line reports us/step (wall clock over the timed steps), the
+dominant kernel's duration (HIP events on its stream) against the HBM
+roofline, and the CPU oracle timed on the host on one full step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+METRIC = ("verify-attention µs/step and achieved HBM GB/s (% peak), "
+          "32K ctx INT4/INT8")
+PEAK_GBPS = 8000.0
+WORKLOAD = "llama3_8b_32k"
+T_VERIFY, T_DRAFT = 7, 1
+N_COPIES = 8
+
+
+def algorithmic_bytes(Hkv, Hq, d, G, Gv, n_q, n_r, T, bits_read):
+    """Bytes one attention launch must move: codes at the bits the path
+    reads per element of K and V, fp16 scale/zero amortized per group,
+    fp16 residual K and V, fp16 q and out."""
+    per_tok = 2 * d * bits_read // 8 + 4 * d // G + 4 * (d // Gv)
+    return Hkv * (n_q * per_tok + n_r * 4 * d) + 2 * T * Hq * d * 2
+
+
+def build_caches(w, seed, device):
+    """N_COPIES device caches holding the first L-7 tokens, plus the host
+    fp16 token streams (B, L, Hkv, d) they were built from."""
+    import torch
+    import kvq_synth as synth
+    import quantized_kv_attention_quant_amd as kq
+    K = np.empty((w.B, w.L, w.Hkv, w.d), np.float16)
+    V = np.empty_like(K)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            K[b, :, h], V[b, :, h] = synth.kv_block(w, seed, b, h, w.L)
+    L0 = w.L - T_VERIFY
+    shape = kq.Shape(B=w.B, Hkv=w.Hkv, d=w.d, G=w.G, Gv=w.Gv, bits=w.bits,
+                     R=w.R, L_max=w.L, max_append=32)
+    base = kq.QuantKVCache(shape, device=device)
+    base.append(torch.from_numpy(np.ascontiguousarray(K[:, :L0])).to(device),
+                torch.from_numpy(np.ascontiguousarray(V[:, :L0])).to(device))
+    torch.cuda.synchronize()
+    caches = [base] + [base.clone() for _ in range(N_COPIES - 1)]
+    torch.cuda.synchronize()
+    return caches, K, V
+
+
+def cpu_baseline(w, seed, K, V, q_draft, q_verify, k_new, v_new):
+    """Time the CPU oracle on one full step (all 8 kv heads): replay the
+    cache, append the 7 tokens, draft + verify attention in float64."""
+    from oracle import attention as oatt
+    from oracle import cache as ocache
+    rep = ocache.Replay(w.B, w.Hkv, w.d, w.G, w.Gv, w.bits, w.R)
+    rep.append(K, V)
+    t0 = time.perf_counter()
+    rep.append(k_new, v_new)
+    oatt.attend(rep, q_draft, "draft4", w.d ** -0.5)
+    oatt.attend(rep, q_verify, "target", w.d ** -0.5)
+    rep.rollback(T_VERIFY)
+    dt = time.perf_counter() - t0
+    return {"value": dt * 1e6, "unit": "us/step", "cores": 1,
+            "kind": "oracle",
+            "sample": "one full step (append 7, INT4 draft T=1, INT8 verify "
+                      "T=7 over all 8 kv heads of the 32K cache), float64 "
+                      "numpy einsum on one host thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the verify path shards by kv head "
+              "with no communication, so --gpus above 1 is not run here",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kvq_synth as synth
+    import quantized_kv_attention_quant_amd as kq
+
+    kq.lib()   # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[WORKLOAD]
+    caches, K, V = build_caches(w, args.seed, dev)
+    L0 = w.L - T_VERIFY
+    Kn = np.ascontiguousarray(K[:, L0:])       # the 7 speculative tokens
+    Vn = np.ascontiguousarray(V[:, L0:])
+    qd16 = synth.queries(w, args.seed, T_DRAFT)
+    qv16 = synth.queries(w, args.seed + 1, T_VERIFY)
+    k_new, v_new = torch.from_numpy(Kn).to(dev), torch.from_numpy(Vn).to(dev)
+    q_draft, q_verify = torch.from_numpy(qd16).to(dev), torch.from_numpy(qv16).to(dev)
+    out_d = torch.empty_like(q_draft)
+    out_v = torch.empty_like(q_verify)
+    ws = caches[0].attn_workspace(T_VERIFY, w.Hq)   # large enough for both
+    assert ws.numel() >= kq.kv_attn_workspace_bytes(caches[0].c, T_DRAFT, w.Hq)
+    sm = w.d ** -0.5
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    n_q, n_r = caches[0].n_q, caches[0].n_r + T_VERIFY
+    bytes_draft = algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv, n_q, n_r,
+                                    T_DRAFT, 4)
+    bytes_verify = algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv, n_q, n_r,
+                                     T_VERIFY, 8)
+    bytes_append = 2 * 2 * T_VERIFY * w.B * w.Hkv * w.d * 2
+
+    events = []
+
+    def step(i, timed):
+        c = caches[i % N_COPIES]
+        if timed:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+        kq.kv_quant_append(c.c, k_new, v_new, T_VERIFY, sh)
+        if timed:
+            e[1].record(stream)
+        kq.kv_attn_verify(c.c, q_draft, T_DRAFT, w.Hq, kq.KVQ_DRAFT4, sm,
+                          out_d, None, ws, sh)
+        if timed:
+            e[2].record(stream)
+        kq.kv_attn_verify(c.c, q_verify, T_VERIFY, w.Hq, kq.KVQ_TARGET, sm,
+                          out_v, None, ws, sh)
+        if timed:
+            e[3].record(stream)
+            events.append(e)
+        kq.kv_rollback(c.c, T_VERIFY)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    # 1) wall clock over K plain steps (no events in the stream)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, False)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    # 2) the same steps with per-kernel HIP events on the launch stream
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    app = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e3
+    drf = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e3
+    ver = np.array([e[2].elapsed_time(e[3]) for e in events]) * 1e3
+    gpu_step = app + drf + ver
+
+    achieved = bytes_verify / (ver.mean() * 1e-6) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(wall * 1e6, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-3-8B GQA layer at 32K: B=1 Hq=32 Hkv=8 d=128 "
+                        "L=32768 G=128 Gv=64 R=256; INT4 draft T=1 + INT8 "
+                        "verify T=7 + append/rollback of 7 tokens",
+            "cache_copies": N_COPIES,
+            "bytes_per_step": bytes_append + bytes_draft + bytes_verify,
+        },
+        "kernels_us": {
+            "append_t7": round(float(np.median(app)), 3),
+            "draft_int4_t1": round(float(np.median(drf)), 3),
+            "verify_int8_t7": round(float(np.median(ver)), 3),
+            "verify_int8_t7_p10_p90": [round(float(np.percentile(ver, 10)), 3),
+                                       round(float(np.percentile(ver, 90)), 3)],
+            "gpu_step_events": round(float(gpu_step.mean()), 3),
+        },
+        "hbm_gbps": {
+            "draft_int4_t1": round(bytes_draft / (drf.mean() * 1e-6) / 1e9, 1),
+            "verify_int8_t7": round(achieved, 1),
+            "step_events": round((bytes_append + bytes_draft + bytes_verify)
+                                 / (gpu_step.mean() * 1e-6) / 1e9, 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kv_attn_verify INT8 T=7",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": bytes_verify,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(
+            w, args.seed, np.ascontiguousarray(K[:, :L0]),
+            np.ascontiguousarray(V[:, :L0]), qd16, qv16, Kn, Vn)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

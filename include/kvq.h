@@ -69,8 +69,10 @@
  *           per = 4/w, lane = 16*g + r,
  *           dword = lane*(d*w/64) + m/per,  bit = 16*h + w*(4*(m%per) + i)
  *       (dword = little-endian u32 index inside the tile).
- *   V scale/zero v_sz: fp16 pairs [B][Hkv][L_max/32][4][8][d/Gv][2] = {s, z};
- *       token j of a tile sits at [g][u] with g = (j%16)/4, u = 4*(j/16)+j%4.
+ *   V scale/zero v_sz: fp16 [B][Hkv][L_max/32][2][4][4][d/Gv][2], per tile
+ *       [part][g][i][group][h] with part 0 = scales, 1 = zero-points: the
+ *       value of token j = 16*h + 4*g + i (h, g, i as above), so each u32
+ *       holds one part of the token pair (4g+i, 16+4g+i) of one group.
  *   Residual ring: slot of absolute token position p is p % ring.
  *     k_res: fp16 [B][Hkv][ring][d], token-major.
  *     v_res: fp16 [B][Hkv][ring/32][32*d], one tile per 32 slots; slot j of

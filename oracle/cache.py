@@ -98,7 +98,7 @@ def device_image(rep: Replay, ring: int):
 
     Returns a dict of per-block arrays (leading dims B, Hkv):
       k_hi, k_lo: u8 (n_q, d*w/8) rows      v_hi, v_lo: u8 (n_q/32, 4*d*w)
-      k_sz: fp16 (n_q/G, d, 2)              v_sz: fp16 (n_q/32, 4, 8, ng, 2)
+      k_sz: fp16 (n_q/G, d, 2)              v_sz: fp16 (n_q/32, 2, 4, 4, ng, 2)
       k_res: fp16 (n_r, d) with slots ``res_slots``
       v_res: fp16 (n_r, d) values of the same slots (read back with
              oracle.layout.unpack_v_res_tile)

@@ -13,8 +13,9 @@ in a plane: 4 for 8-bit codes split into hi/lo nibble planes, else 2 or 1):
   V plane tile  u8 [4*d*w] per 32 tokens; token j, channel c:
                 g=(j%16)//4, i=j%4, h=j//16, r=c%16, m=c//16, per=4//w,
                 u32 index (16g+r)*(d*w//64) + m//per, bit 16h + w*(4*(m%per)+i).
-  V scale/zero  fp16 [L_max/32][4][8][d/Gv][2]; token j at
-                [(j%16)//4][4*(j//16) + j%4].
+  V scale/zero  fp16 [L_max/32][2][4][4][d/Gv][2] per tile, indexed
+                [part][g][i][group][h]: part 0 = scales, 1 = zero-points,
+                token j = 16h + 4g + i.
   k_res         fp16 [ring][d], slot = position % ring.
   v_res tile    fp16 [32*d] per 32 slots; slot j, channel c at half index
                 (16g+r)*(d//2) + 8m + 2i + h.
@@ -128,30 +129,33 @@ def unpack_k_sz(raw: np.ndarray):
     return raw[..., 0].copy(), raw[..., 1].copy()
 
 
-def _v_sz_perm():
-    """Position of tile token j inside the [4][8] token grid."""
+def _v_sz_index():
+    """(g, i, h) of tile token j for the scale/zero planes."""
     j = np.arange(32)
-    g = (j % 16) // 4
-    u = 4 * (j // 16) + j % 4
-    return g * 8 + u
+    return (j % 16) // 4, j % 4, j // 16
 
 
 def pack_v_sz(s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """(N, d/Gv) s, z -> fp16 (N/32, 4, 8, d/Gv, 2)."""
+    """(N, d/Gv) s, z -> fp16 (N/32, 2, 4, 4, d/Gv, 2)."""
     N, ng = s.shape
     nt = N // 32
-    pos = _v_sz_perm()
-    pairs = np.stack([s.astype(np.float16), z.astype(np.float16)], axis=-1)
-    out = np.empty((nt, 32, ng, 2), np.float16)
-    out[:, pos] = pairs.reshape(nt, 32, ng, 2)
-    return out.reshape(nt, 4, 8, ng, 2)
+    st = s.reshape(nt, 32, ng).astype(np.float16)
+    zt = z.reshape(nt, 32, ng).astype(np.float16)
+    out = np.empty((nt, 2, 4, 4, ng, 2), np.float16)
+    for j, (g, i, h) in enumerate(zip(*_v_sz_index())):
+        out[:, 0, g, i, :, h] = st[:, j]
+        out[:, 1, g, i, :, h] = zt[:, j]
+    return out
 
 
 def unpack_v_sz(raw: np.ndarray):
-    nt, _, _, ng, _ = raw.shape
-    flat = raw.reshape(nt, 32, ng, 2)[:, _v_sz_perm()]
-    return (flat[..., 0].reshape(nt * 32, ng).copy(),
-            flat[..., 1].reshape(nt * 32, ng).copy())
+    nt, _, _, _, ng, _ = raw.shape
+    s = np.empty((nt, 32, ng), np.float16)
+    z = np.empty_like(s)
+    for j, (g, i, h) in enumerate(zip(*_v_sz_index())):
+        s[:, j] = raw[:, 0, g, i, :, h]
+        z[:, j] = raw[:, 1, g, i, :, h]
+    return s.reshape(nt * 32, ng), z.reshape(nt * 32, ng)
 
 
 # ---- residual V ring tiles ----------------------------------------------------

@@ -108,8 +108,10 @@ Plan plan_attn(const kvq_cache* c, int T, int Hq) {
   return p;
 }
 
+// Two u32 counters per block (split tickets, finished merges), zero between
+// calls.
 size_t ticket_bytes(const kvq_cache* c) {
-  return (size_t)round_up((int64_t)c->B * c->Hkv * 4, 256);
+  return (size_t)round_up((int64_t)c->B * c->Hkv * 8, 256);
 }
 
 }  // namespace
@@ -237,6 +239,7 @@ KVQ_API int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq,
   a.s_r = p.s_r;
   a.s_alloc = p.s_alloc;
   a.rows_pad = p.rows_pad;
+  a.ngr = c->G >= 128 ? 1 : 128 / c->G;
   hipError_t e = kvq::launch_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_attn_verify launch");
   return KVQ_OK;

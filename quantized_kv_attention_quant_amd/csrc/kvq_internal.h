@@ -114,6 +114,7 @@ struct AttnArgs {
   int s_q;          // quantized-split workgroups per block
   int s_r;          // residual workgroups per block
   int s_alloc;      // partial slots per block in the workspace
+  int ngr;          // key groups per round of 4 tiles: max(1, 128/G)
   int rows_pad;     // 16 * row tiles
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);

@@ -151,10 +151,13 @@ __device__ void value_tile(const AppendArgs& a, int item, int b, int kvh,
       mx = fmaxf(mx, x);
     }
     const float z = mn, s = stored_scale(mn, mx, Lv);
-    const int gg = (j & 15) >> 2, u = 4 * (j >> 4) + (j & 3);
-    a.p.v_sz[blk * g.vsz_block + tile * g.vsz_tile + (gg * 8 + u) * ng + grp] =
-        __halves2half2(__float2half_rn(s), __float2half_rn(z));
-    const int per = 4 / g.w, i = j & 3, h = j >> 4;
+    const int gg = (j & 15) >> 2, i = j & 3, h = j >> 4;
+    // [part][g][i][group][h]: scale plane then zero-point plane
+    __half* sz = (__half*)(a.p.v_sz + blk * g.vsz_block + tile * g.vsz_tile);
+    const int at = ((gg * 4 + i) * ng + grp) * 2 + h;
+    sz[at] = __float2half_rn(s);
+    sz[32 * ng + at] = __float2half_rn(z);
+    const int per = 4 / g.w;
     for (int c = grp * g.Gv; c < (grp + 1) * g.Gv; ++c) {
       unsigned q = code_of(value_at(a, b, kvh, p, c), z, s, Lv);
       const int r = c & 15, m = c >> 4;

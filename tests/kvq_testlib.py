@@ -70,7 +70,7 @@ def read_block(cache: kq.QuantKVCache, b: int, h: int):
     ng = d // s.Gv
     vsz_tile = 32 * ng * 4
     vsz = sl(cache.v_sz, (s.L_max // 32) * vsz_tile, 0, nt * vsz_tile)
-    vs, vz = layout.unpack_v_sz(vsz.view(np.float16).reshape(nt, 4, 8, ng, 2))
+    vs, vz = layout.unpack_v_sz(vsz.view(np.float16).reshape(nt, 2, 4, 4, ng, 2))
     res_b = ring * d * 2
     kr_all = sl(cache.k_res, res_b, 0, res_b).view(np.float16).reshape(ring, d)
     vr_all = sl(cache.v_res, res_b, 0, res_b).view(np.float16).reshape(

@@ -91,7 +91,7 @@ def test_device_image_shapes():
     img = cache.device_image(rep, ring=288)
     assert img["k_hi"].shape == (1, 2, 384, 64)
     assert img["v_lo"].shape == (1, 2, 12, 4 * 128 * 4)
-    assert img["v_sz"].shape == (1, 2, 12, 4, 8, 2, 2)
+    assert img["v_sz"].shape == (1, 2, 12, 2, 4, 4, 2, 2)
     # 600 tokens, R=256, G=128: ceil(344/128) = 3 groups flushed
     assert (rep.n_q, rep.n_r) == (384, 216)
     assert img["res_slots"].tolist() == [(384 + i) % 288 for i in range(216)]

@@ -84,12 +84,14 @@ def test_v_sz_round_trip_and_position():
     s = rng.standard_normal((64, 2)).astype(np.float16)
     z = rng.standard_normal((64, 2)).astype(np.float16)
     raw = layout.pack_v_sz(s, z)
-    assert raw.shape == (2, 4, 8, 2, 2)
+    assert raw.shape == (2, 2, 4, 4, 2, 2)
     s2, z2 = layout.unpack_v_sz(raw)
     assert np.array_equal(s2, s) and np.array_equal(z2, z)
-    # token 21 of tile 1 (j=21): g=(21%16)//4=1, u=4*1+1=5
-    assert raw[1, 1, 5, 0, 0] == s[32 + 21, 0]
-    assert raw[1, 1, 5, 1, 1] == z[32 + 21, 1]
+    # token 21 of tile 1: g = (21 % 16) // 4 = 1, i = 1, h = 1
+    assert raw[1, 0, 1, 1, 0, 1] == s[32 + 21, 0]
+    assert raw[1, 1, 1, 1, 1, 1] == z[32 + 21, 1]
+    # token 5 shares that u32 as its low half (g = 1, i = 1, h = 0)
+    assert raw[1, 0, 1, 1, 0, 0] == s[32 + 5, 0]
 
 
 def test_v_res_tile_round_trip_and_position():
