@@ -136,8 +136,8 @@ typedef struct kvq_cache {
 /* Validate the shape, derive `ring` and the byte size of every buffer, and
  * set n_q = n_r = 0.  Host only.  Shape rules: B, Hkv >= 1; d in {64, 128};
  * bits in {8, 2, 1} (bits == 1 needs d == 128); G a positive multiple of
- * 32; L_max a positive multiple of G; Gv a multiple of 16 dividing d with
- * d/Gv <= 4; G <= R; 1 <= max_append.  The ring needs no initial contents.
+ * 32; L_max a positive multiple of G, at most 2^24; Gv a multiple of 16
+ * dividing d with d/Gv <= 4; G <= R; 1 <= max_append.  The ring needs no initial contents.
  * KVQ_EINVAL (message in kv_last_error) when a rule fails. */
 int kv_cache_layout(kvq_cache* c);
 

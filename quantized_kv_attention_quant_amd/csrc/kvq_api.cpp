@@ -27,7 +27,6 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr int kWavesPerGroup = 4;      // attention workgroup = 4 waves
-constexpr int kTargetGroups = 512;     // ~2 workgroups per CU on 256 CUs
 constexpr int kTopkChunk = 1024;       // tokens per top-k workgroup
 constexpr int kMaxTopk = 256;
 
@@ -45,6 +44,8 @@ int check_shape(const kvq_cache* c) {
   if (c->G < 32 || c->G % 32) return fail(KVQ_EINVAL, "G must be a multiple of 32");
   if (c->L_max < c->G || c->L_max % c->G)
     return fail(KVQ_EINVAL, "L_max must be a positive multiple of G");
+  if (c->L_max > (1LL << 24))
+    return fail(KVQ_EINVAL, "L_max must be <= 2^24 tokens");
   if (c->Gv < 16 || c->Gv % 16 || c->d % c->Gv || c->d / c->Gv > 4)
     return fail(KVQ_EINVAL,
                 "Gv must be a multiple of 16 dividing d with d/Gv <= 4");
@@ -76,36 +77,26 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 // ---- attention split plan --------------------------------------------------
-struct Plan {
-  int rows, rows_pad, tpw, s_q, s_r, s_alloc;
-};
+// The launcher picks the split count per block from the device's resident
+// workgroup slots (plan_splits); the workspace holds one partial per split,
+// sized for up to kSlotsBound slots (256 CUs x 2 workgroups) and never more
+// splits than the cache has units of work for.
+constexpr int kSlotsBound = 512;
+constexpr int kMaxSplits = 1024;   // (m, l) of each split fit the merge LDS
 
-int s_target(const kvq_cache* c) {
-  const int64_t blocks = (int64_t)c->B * c->Hkv;
-  int64_t t = cdiv(kTargetGroups, blocks);
-  const int64_t cap = 2LL * c->d - cdiv(cdiv(c->ring, 32), kWavesPerGroup);
-  if (t > cap) t = cap;
-  return t < 1 ? 1 : (int)t;
+int rows_pad_of(int T, int Hq, int Hkv) {
+  return T * (Hq / Hkv) <= 16 ? 16 : 32;
 }
 
 int s_alloc_of(const kvq_cache* c) {
-  return s_target(c) + (int)cdiv(cdiv(c->ring, 32), kWavesPerGroup);
-}
-
-Plan plan_attn(const kvq_cache* c, int T, int Hq) {
-  Plan p;
-  const int gs = Hq / c->Hkv;
-  p.rows = T * gs;
-  p.rows_pad = p.rows <= 16 ? 16 : 32;
-  const int64_t nqt = c->n_q / 32;
-  const int st = s_target(c);
-  p.tpw = (int)(nqt <= (int64_t)kWavesPerGroup * st
-                    ? 1
-                    : cdiv(nqt, (int64_t)kWavesPerGroup * st));
-  p.s_q = (int)cdiv(nqt, (int64_t)kWavesPerGroup * p.tpw);
-  p.s_r = (int)cdiv(cdiv(c->n_r, 32), kWavesPerGroup);
-  p.s_alloc = s_alloc_of(c);
-  return p;
+  const int64_t nb = (int64_t)c->B * c->Hkv;
+  const int64_t ring = round_up((int64_t)c->R + c->max_append, 32);
+  const int64_t units_max = 2 * cdiv(ring, 32) + cdiv(c->L_max, 32);
+  int64_t s = 4 * cdiv(kSlotsBound, nb);
+  const int64_t by_units = cdiv(units_max, kWavesPerGroup);
+  if (s > by_units) s = by_units;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
 }
 
 // Two u32 counters per block (split tickets, finished merges), zero between
@@ -187,10 +178,8 @@ KVQ_API int kv_rollback(kvq_cache* c, int m) {
 
 KVQ_API size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq) {
   if (check_shape(c) || T < 1 || Hq < 1 || Hq % c->Hkv) return 0;
-  const int rows = T * (Hq / c->Hkv);
-  const int rows_pad = rows <= 16 ? 16 : 32;
-  return ticket_bytes(c) + (size_t)c->B * c->Hkv * s_alloc_of(c) * rows_pad *
-                               (c->d + 2) * sizeof(float);
+  return (size_t)c->B * c->Hkv * s_alloc_of(c) * rows_pad_of(T, Hq, c->Hkv) *
+         (c->d + 2) * sizeof(float);
 }
 
 KVQ_API int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq,
@@ -216,30 +205,24 @@ KVQ_API int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq,
   if (!ws || ws_bytes < need)
     return fail(KVQ_EWORKSPACE, "workspace needs %zu bytes", need);
 
-  const Plan p = plan_attn(c, T, Hq);
   kvq::AttnArgs a;
   a.g = kvq::geom_of(c);
   a.p = kvq::ptrs_of(c);
   a.q = (const __half*)q;
   a.out = (__half*)out;
   a.lse = lse;
-  a.tickets = (unsigned*)ws;
-  a.ws = (float*)((char*)ws + ticket_bytes(c));
+  a.ws = (float*)ws;
   a.n_q = c->n_q;
   a.n_r = c->n_r;
   a.T = T;
   a.Hq = Hq;
   a.gs = Hq / c->Hkv;
-  a.rows = p.rows;
+  a.rows = T * a.gs;
   a.path = path;
   a.c0 = sm_scale * 1.4426950408889634f;
-  a.waves = kWavesPerGroup;
-  a.tpw = p.tpw;
-  a.s_q = p.s_q;
-  a.s_r = p.s_r;
-  a.s_alloc = p.s_alloc;
-  a.rows_pad = p.rows_pad;
-  a.ngr = c->G >= 128 ? 1 : 128 / c->G;
+  a.S = 0;
+  a.s_alloc = s_alloc_of(c);
+  a.rows_pad = rows_pad_of(T, Hq, c->Hkv);
   hipError_t e = kvq::launch_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_attn_verify launch");
   return KVQ_OK;

@@ -7,30 +7,40 @@
 // log-sum-exp).  SpeCache page, Approach: output + speculative token (T = 2)
 // over a 1/2-bit KIVI copy.
 //
-// Work decomposition (grid = splits x Hkv x B, 4 waves per workgroup):
-//   * quantized splits: each wave walks a run of 32-token tiles of the
-//     quantized prefix; residual splits: each wave takes one 32-slot tile of
-//     the fp16 ring (where the causal mask among the T query tokens lives).
+// Work decomposition (grid = splits x Hkv x B, NW waves per workgroup):
+//   * a block's work is a sequence of units: two per 32-slot tile of the fp16
+//     ring (its K, then its V, 8 KB each at d = 128) followed by the
+//     quantized prefix in units of TPU 32-token tiles (codes, value
+//     scale/zero and the key scale/zero of the tile's group).  Every wave of
+//     the grid owns one contiguous run of units (a ring tile's two units never
+//     split), so waves never wait for each other inside the loop.
+//   * each wave streams its units through a private ring of ST stages in
+//     LDS with direct global->LDS loads (global_load_lds_dwordx4, issued
+//     ST-1 units ahead, counted with vmcnt), so the bytes in flight are not
+//     held in registers.
 //   * per tile the wave computes S^T = K * Q'^T on MFMA (16x16x32 f16, two
-//     16-token subtiles x up to two 16-row tiles), runs the online softmax on
-//     the S^T accumulators in place, and feeds P'^T straight back as the B
+//     16-token subtiles x one or two 16-row tiles), runs the online softmax
+//     on the S^T accumulators in place and feeds P'^T straight back as the B
 //     operand of O^T += V^T * P'^T: the accumulator layout of the score MFMA
-//     (lane = row, 4 consecutive tokens) is exactly the operand layout the PV
-//     MFMA needs once the V tile is stored token-permuted, so no data crosses
-//     lanes.  Rows are query tokens x GQA heads (T * Hq/Hkv <= 32).
-//   * codes are turned into fp16 MFMA operands in registers with the
-//     "0x6400 | code" trick (fp16 1024 + code); per-channel key scales are
-//     folded into Q' = q * s * sm_scale * log2(e) once per key group, kept as
-//     two fp16 parts (hi + lo, two MFMAs) so the scores carry ~22 bits of Q'
-//     (one fp16 part alone moves outlier-channel logits by ~1e-2); the 1024
-//     offset and the zero-points go into the accumulator's initial value; per-
-//     token value scales are folded into P' = p * s * 2^10 and value zero-
-//     points into a per-row fp32 side sum.
-//   * the 4 waves merge in registers through LDS and write one partial
+//     (lane = row, 4 consecutive tokens) is the operand layout the PV MFMA
+//     needs once V is stored token-permuted, so no data crosses lanes.  Rows
+//     are query tokens x GQA heads (T * Hq/Hkv <= 32).
+//   * codes become fp16 MFMA operands in registers with the "0x6400 | code"
+//     trick (fp16 1024 + code).  Per-channel key scales are folded into
+//     Q' = q * s * sm_scale * log2(e) once per key group, kept as two fp16
+//     parts (hi + lo, two MFMAs) so the scores carry ~22 bits of Q'; the 1024
+//     offset (an MFMA of a constant operand with Q') and the zero-points go
+//     into the accumulator's initial value.  Per-token value scales are
+//     folded into P' = p * s * 2^7, value zero-points and the 1024 offset
+//     into a per-row fp32 side sum (packed fp16 dot products).
+//   * the softmax reference moves lazily: scores are taken relative to the
+//     row's reference (folded into the accumulator's initial value) and the
+//     reference is only raised when a score exceeds it by more than 2^3, so
+//     the common tile needs no cross-lane reduction and no rescale.
+//   * the waves of a workgroup merge through LDS and write one partial
 //     (m, l, o) per workgroup.  A second launch, one workgroup per (block,
-//     row), merges that row's partials by log-sum-exp in parallel (fp16
-//     output, natural-log LSE); the kernel boundary makes the partials
-//     visible, so the split kernel needs no device-scope fence or ticket.
+//     row), merges that row's partials by log-sum-exp (fp16 output, natural-
+//     log LSE); the kernel boundary makes the partials visible.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -40,15 +50,19 @@ typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef unsigned u4v __attribute__((ext_vector_type(4)));
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
 
-constexpr int NW = 4;
-constexpr int NT = NW * kWave;
 constexpr unsigned kMagic = 0x64006400u;       // fp16 pair (1024, 1024)
 constexpr unsigned kMinus1024 = 0xE400E400u;   // fp16 pair (-1024, -1024)
 constexpr unsigned kMinusDraft = 0xE3F1E3F1u;  // fp16 pair (-1016.5, -1016.5)
-constexpr float kPExp = 10.f;                  // P' = p * s * 2^10
-constexpr float kPScale = 1024.f;
+// Probabilities are taken as 2^(s - m_ref + kPExp) with s <= m_ref + kTau
+// between reference moves: p' <= 2^10, and P' = p' * s_v stays an fp16
+// normal for value scales up to 64.
+constexpr float kPExp = 7.f;
+constexpr float kTau = 3.f;
+constexpr float kOScale = 1.f / 128.f;         // 2^-kPExp
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr int kLdsBytes = 160 * 1024;
 
 enum Path { P_T8 = 0, P_D4 = 1, P_L2 = 2, P_L1 = 3 };
 
@@ -60,6 +74,17 @@ __device__ __forceinline__ f4v mfma16(u4v a, u4v b, f4v c) {
 __device__ __forceinline__ unsigned hadd2(unsigned x, unsigned y) {
   h2v r = __builtin_bit_cast(h2v, x) + __builtin_bit_cast(h2v, y);
   return __builtin_bit_cast(unsigned, r);
+}
+
+__device__ __forceinline__ unsigned hmul2(unsigned x, unsigned y) {
+  h2v r = __builtin_bit_cast(h2v, x) * __builtin_bit_cast(h2v, y);
+  return __builtin_bit_cast(unsigned, r);
+}
+
+// fp32 += x.lo * y.lo + x.hi * y.hi (fp16 pairs, products exact in fp32)
+__device__ __forceinline__ float dot2(unsigned x, unsigned y, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, x),
+                                __builtin_bit_cast(h2v, y), acc, false);
 }
 
 __device__ __forceinline__ unsigned pack2(float lo, float hi) {
@@ -75,13 +100,18 @@ __device__ __forceinline__ float h_lo(unsigned x) {
 __device__ __forceinline__ float h_hi(unsigned x) {
   return (float)__builtin_bit_cast(h2v, x)[1];
 }
+// fp16 element j of a pair of dwords (4 halves)
+__device__ __forceinline__ float h_at(u2v x, int j) {
+  return j < 2 ? (j == 0 ? h_lo(x[0]) : h_hi(x[0]))
+               : (j == 2 ? h_lo(x[1]) : h_hi(x[1]));
+}
 
 // The fp32 value as materialised in a register.  Splitting x into fp16
 // hi = fp16(x) and lo = fp16(x - hi) needs both parts to see the same x,
 // but the compiler may fold a product feeding an fp16 conversion into one
-// mixed-precision FMA (v_fma_mixlo_f16, a single rounding of the exact
-// product) for one use and round the fp32 product for the other; on an
-// fp16 rounding midpoint the two differ and lo gets the wrong sign.
+// mixed-precision FMA (a single rounding of the exact product) for one use
+// and round the fp32 product for the other; on an fp16 rounding midpoint
+// the two differ and lo gets the wrong sign.
 __device__ __forceinline__ float opaque(float x) {
   asm volatile("" : "+v"(x));
   return x;
@@ -91,18 +121,24 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
-// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
-// l^48), with the ds_bpermute byte addresses computed once by the caller.
-__device__ __forceinline__ float bperm(int addr, float v) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48) with the lane-swap permutes: the operands are combined in the same
+// order on every lane, so all four get bit-identical results.
+__device__ __forceinline__ float max_x4(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v),
+                                            __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v),
+                                            __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
-__device__ __forceinline__ float xor_max(float v, int a16, int a32) {
-  v = fmaxf(v, bperm(a16, v));
-  return fmaxf(v, bperm(a32, v));
-}
-__device__ __forceinline__ float xor_sum(float v, int a16, int a32) {
-  v += bperm(a16, v);
-  return v + bperm(a32, v);
+__device__ __forceinline__ float sum_x4(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v),
+                                            __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v),
+                                            __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 // Decode constants held in registers: gfx9 VOP3 forms (v_and_or_b32,
@@ -133,10 +169,18 @@ __device__ __forceinline__ DecK dec_consts() {
 // token n of the dword).  Pair j = nibbles (j, j+4) as fp16 (1024 + code):
 // two bit-field inserts build the bytes hi<<4|lo of the even and odd
 // nibbles, four byte permutes place them under the 0x64 exponent byte.
+// (m & a) | (~m & b) in one instruction; the compiler splits the pattern
+// into an and plus an and-or.
+__device__ __forceinline__ unsigned bfi(unsigned m, unsigned a, unsigned b) {
+  unsigned r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(m), "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ void dec8(unsigned H, unsigned L, unsigned* r,
                                      const DecK& k) {
-  const unsigned ce = (k.m_hi & (H << 4)) | (~k.m_hi & L);
-  const unsigned co = (k.m_hi & H) | (~k.m_hi & (L >> 4));
+  const unsigned ce = bfi(k.m_hi, H << 4, L);
+  const unsigned co = bfi(k.m_hi, H, L >> 4);
   r[0] = __builtin_amdgcn_perm(k.magic_b, ce, 0x05020500u);
   r[1] = __builtin_amdgcn_perm(k.magic_b, co, 0x05020500u);
   r[2] = __builtin_amdgcn_perm(k.magic_b, ce, 0x05030501u);
@@ -159,56 +203,143 @@ __device__ __forceinline__ unsigned declow(unsigned H, int i, const DecK& k) {
 }
 
 template <int N>
-__device__ __forceinline__ void ldg(const void* p, unsigned* o) {
+__device__ __forceinline__ void lds_read(const unsigned char* p, unsigned* o) {
   if constexpr (N == 1) {
     o[0] = *(const unsigned*)p;
   } else if constexpr (N == 2) {
-    uint2 v = *(const uint2*)p;
-    o[0] = v.x; o[1] = v.y;
+    const u2v v = *(const u2v*)p;
+    o[0] = v[0]; o[1] = v[1];
   } else {
     static_assert(N % 4 == 0, "dword count");
 #pragma unroll
     for (int k = 0; k < N / 4; ++k) {
-      uint4 v = ((const uint4*)p)[k];
-      o[4 * k] = v.x; o[4 * k + 1] = v.y; o[4 * k + 2] = v.z; o[4 * k + 3] = v.w;
+      const u4v v = ((const u4v*)p)[k];
+      o[4 * k] = v[0]; o[4 * k + 1] = v[1]; o[4 * k + 2] = v[2]; o[4 * k + 3] = v[3];
     }
   }
 }
 
-template <int PATH, int D, int NRT, int NG>
+// ---- direct global -> LDS copies --------------------------------------------
+// One instruction moves 16 bytes per lane: lane l's bytes g + voff land at
+// LDS address M0 + 16 l.  The compiler does not see these loads (it would
+// wait for every pending one before any LDS read), so the copies are counted
+// by hand with s_waitcnt vmcnt; M0 is restored after each one.
+__device__ __forceinline__ void dma16(const void* gp, unsigned voff,
+                                      unsigned lds) {
+  // the base must sit in SGPRs: it is wave-uniform by construction.
+  // readfirstlane returns int: zero-extend each half (a sign-extended low
+  // half would set the upper address bits)
+  const uint64_t gi = (uint64_t)(uintptr_t)gp;
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)gi);
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(gi >> 32));
+  const uint64_t g = lo | (hi << 32);
+  unsigned save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(voff), "s"(g)
+      : "memory");
+}
+
+constexpr int dma_count(int bytes) { return (bytes + 1023) / 1024; }
+
+// Copy BYTES (a multiple of 16) from g to LDS address lds: dma_count(BYTES)
+// instructions, the last one on the first (BYTES % 1024) / 16 lanes.
+template <int BYTES>
+__device__ __forceinline__ void dma(const unsigned char* g, unsigned lds,
+                                    unsigned lane16) {
+  static_assert(BYTES % 16 == 0, "16-byte pieces");
+#pragma unroll
+  for (int k = 0; k < BYTES / 1024; ++k) dma16(g + 1024 * k, lane16, lds + 1024 * k);
+  if constexpr (BYTES % 1024 != 0) {
+    constexpr int full = BYTES / 1024 * 1024;
+    if (lane16 < (unsigned)(BYTES % 1024)) dma16(g + full, lane16, lds + full);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `pending` copies are outstanding, rounded down to one
+// of the counts K*A or K*B (K < ST); waiting for more than needed is safe.
+template <int A, int B, int K>
+__device__ __forceinline__ void wait_le(int pending) {
+  if constexpr (K == 0) {
+    wait_vm<0>();
+  } else {
+    constexpr int hi = K * A > K * B ? K * A : K * B;
+    constexpr int lo = K * A > K * B ? K * B : K * A;
+    if (pending >= hi) { wait_vm<hi>(); return; }
+    if (pending >= lo) { wait_vm<lo>(); return; }
+    wait_le<A, B, K - 1>(pending);
+  }
+}
+
+// Per-path geometry.  Every wave owns one 16-row tile of the block's rows.
+// Up to 16 rows (SOLO) every wave streams its own run of units; with 17..32
+// rows (PAIR) two waves share one stream, wave h of the pair taking rows
+// 16h .. 16h+15, so the per-wave state (B operands, accumulators) is that
+// of 16 rows and two waves fit on every SIMD.
+template <int PATH, int D, int NG, bool PAIR>
 struct Cfg {
+  static constexpr int NH = PAIR ? 2 : 1;        // row tiles per stream
+  static constexpr int RP = 16 * NH;             // staged (padded) rows
   static constexpr int W = PATH == P_L2 ? 2 : PATH == P_L1 ? 1 : 4;
-  static constexpr bool TWO = PATH == P_T8;   // hi + lo planes
-  static constexpr int KS = D / 32;           // MFMA k-steps per subtile
-  static constexpr int NDK = D * W / 128;     // K dwords / lane / plane / subtile
-  static constexpr int NDV = D * W / 64;      // V dwords / lane / plane / tile
-  static constexpr int MT = D / 16;           // 16-channel output tiles
-  static constexpr int PERK = 16 / W;         // code pairs per K dword
-  static constexpr int RP = 16 * NRT;         // padded rows
-  static constexpr int NSZ = 8 * NG;          // V scale dwords / lane / tile
+  static constexpr bool TWO = PATH == P_T8;      // hi + lo planes
+  static constexpr bool LOW = PATH == P_L2 || PATH == P_L1;
+  static constexpr int KS = D / 32;              // MFMA k-steps per subtile
+  static constexpr int NDK = D * W / 128;        // K dwords / lane / plane / subtile
+  static constexpr int NDV = D * W / 64;         // V dwords / lane / plane / tile
+  static constexpr int MT = D / 16;              // 16-channel output tiles
   static constexpr float KBIAS =
       PATH == P_T8 ? 1024.f : PATH == P_D4 ? 1016.5f : 0.f;
-};
-
-template <class C>
-struct QTile {
-  unsigned kh[2][C::NDK];
-  unsigned kl[2][C::TWO ? C::NDK : 1];
-  unsigned vh[C::NDV];
-  unsigned vl[C::TWO ? C::NDV : 1];
-  unsigned sz[C::NSZ];
+  static constexpr unsigned NEG = PATH == P_D4 ? kMinusDraft : kMinus1024;
+  // stage layout of one quantized tile (bytes)
+  static constexpr int PL = 4 * D * W;           // one code plane
+  static constexpr int VSZB = 128 * NG;          // value scale/zero pairs
+  static constexpr int KSZB = 4 * D;             // key scale/zero of a group
+  static constexpr int O_KH = 0, O_KL = PL;
+  static constexpr int O_VH = TWO ? 2 * PL : PL, O_VL = O_VH + PL;
+  static constexpr int O_VSZ = TWO ? 4 * PL : 2 * PL;
+  static constexpr int O_KSZ = O_VSZ + VSZB;
+  static constexpr int TILE = O_KSZ + KSZB;
+  static constexpr int RESU = 64 * D;            // fp16 K or V of a ring tile
+  static constexpr int TPU = (RESU + TILE - 1) / TILE;
+  static constexpr int STAGE = TPU * TILE;
+  static constexpr int NI_TILE =
+      (TWO ? 4 : 2) * dma_count(PL) + dma_count(VSZB) + dma_count(KSZB);
+  static constexpr int NIQ = TPU * NI_TILE;
+  static constexpr int NIR = dma_count(RESU);
+  static constexpr int QB = RP * D * 2;          // staged q rows (fp16)
+  // waves per workgroup: 8 (two per SIMD) unless eight solo streams of two
+  // stages do not fit the LDS
+  static constexpr int NW = PAIR || 16 * STAGE + QB <= kLdsBytes ? 8 : 4;
+  static constexpr int NS = PAIR ? NW / 2 : NW;  // unit streams per workgroup
+  static constexpr int ST0 = (kLdsBytes - QB) / (NS * STAGE);
+  static constexpr int ST = ST0 > 4 ? 4 : ST0;
+  static constexpr int LDS = NS * ST * STAGE + QB;
+  static constexpr int MERGE = (NS / 2) * NH * 16 * (D + 4 + 2) * 4;
+  static_assert(ST >= (PAIR ? 3 : 2), "stages per stream");
+  static_assert((ST - 1) * (NIQ > NIR ? NIQ : NIR) <= 63, "vmcnt range");
+  static_assert(MERGE <= NS * ST * STAGE, "merge slabs fit the stage area");
 };
 
 // Merge kernel, one workgroup per (block, row): combines the row's S split
 // partials by log-sum-exp with every thread busy: per-split (m, l) into LDS,
 // wave reductions for the row max and sum, then the o rows summed by NT/D
-// thread groups, each with 8 loads in flight.  Runs as a second launch so
-// the partials are visible without device-scope fences in the split kernel.
+// thread groups, each with 8 loads in flight.
 template <int D, int RP>
-__global__ void __launch_bounds__(NT) merge_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
+  constexpr int NT = 256;
   constexpr int NPART = NT / D;          // thread groups over the splits
   __shared__ float lds[2 * 1024 + 8 + NT];
-  const int S = a.s_q + a.s_r;
+  const int S = a.S;
   const int64_t blk = blockIdx.x / a.rows;
   const int row = (int)(blockIdx.x % a.rows);
   const int tid = threadIdx.x, wave = tid / kWave;
@@ -267,625 +398,693 @@ __global__ void __launch_bounds__(NT) merge_kernel(const AttnArgs a) {
     a.lse[((int64_t)b * a.Hq + h) * a.T + t] = (M + __log2f(lsum)) * kLn2;
 }
 
-// Dynamic LDS of the split kernel (the host sizes it):
-//   s_qc   float [RP][D]                       q * sm_scale * log2(e)
-//   s_bq   u4v   [ngr][NRT][KS][2][64]         B operands Q' = hi + lo of the
-//                                              ngr key groups of one round,
-//                                              in MFMA lane order
-//   s_bias float [ngr][RP]                     accumulator start per row
-//   s_ksz  half2 [2][ngr][D]                   key scale/zero of the current
-//                                              and the next round's groups
-// After the tile loop the same bytes hold the wave-merge slabs
-//   slab float [2][RP][D], ml float [2][2][RP].
-template <int RP, int D, int NRT, int KS>
-struct Lds {
-  static size_t bytes(int ngr) {
-    const size_t loop = (size_t)RP * D * 4 + (size_t)ngr * NRT * KS * 2 * 64 * 16 +
-                        (size_t)ngr * RP * 4 + (size_t)2 * ngr * D * 4;
-    const size_t merge = (size_t)2 * RP * D * 4 + 4 * RP * 4;
-    return loop > merge ? loop : merge;
-  }
-};
-
-template <int PATH, int D, int NRT, int NG>
-__global__ void __launch_bounds__(NT) attn_kernel(const AttnArgs a) {
-  using C = Cfg<PATH, D, NRT, NG>;
-  constexpr int RP = C::RP, KS = C::KS, MT = C::MT;
+// Dynamic LDS of the split kernel:
+//   stages  [NS][ST][STAGE]   each stream's ring of units
+//   s_q     fp16 [RP][D]      this block's query rows (zero past `rows`)
+// After the unit loop the stage area holds the stream-merge slabs
+//   slab float [NS/2][NH][16][D+4], ml float [NS/2][NH][2][16].
+template <int PATH, int D, int NG, bool PAIR>
+__global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
+  using C = Cfg<PATH, D, NG, PAIR>;
+  constexpr int KS = C::KS, MT = C::MT, ST = C::ST, NS = C::NS, NH = C::NH;
+  constexpr int RP = C::RP;
+  constexpr int NT = C::NW * kWave;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int ngr = a.ngr;
-  float* s_qc = (float*)smem;
-  u4v* s_bq = (u4v*)(smem + RP * D * 4);
-  float* s_bias = (float*)(smem + RP * D * 4 + (size_t)ngr * NRT * KS * 2 * 64 * 16);
-  unsigned* s_ksz = (unsigned*)(s_bias + ngr * RP);
 
   const CacheGeom& g = a.g;
-  const int S = a.s_q + a.s_r;
-  const int64_t wg = blockIdx.x;
-  const int64_t blk = wg / S;
-  const int split = (int)(wg % S);
+  const int S = a.S;
+  const int64_t blk = blockIdx.x / S;
+  const int split = (int)(blockIdx.x % S);
   const int b = (int)(blk / g.Hkv), kvh = (int)(blk % g.Hkv);
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int l16 = lane & 15, gq = lane >> 4;
-  const int a16 = (lane ^ 16) << 2, a32 = (lane ^ 32) << 2;
-  const int64_t L = a.n_q + a.n_r;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int strm = PAIR ? wave >> 1 : wave;      // stream in the workgroup
+  const int h = PAIR ? wave & 1 : 0;             // row tile of this wave
+  const bool loader = h == 0;                    // issues the stream's copies
+  const int lane = tid % kWave, l16 = lane & 15, gq = lane >> 4;
+  const int row = l16 + 16 * h;                  // this lane's row
+  const unsigned lane16 = 16u * lane;
+  const int L = (int)(a.n_q + a.n_r);
 
-  // Cooperative B-operand build: Q' (or q * c0 when sz == nullptr) of
-  // `slots` key groups, split into fp16 hi + lo, in the lane order of the
-  // score MFMA; s_bias gets  sum_c qc*z - KBIAS * sum_c Q'  per row.  A
-  // power-of-two run of consecutive threads shares a (slot, row) and reduces
-  // with shuffles in a fixed order, so the result is deterministic.  `pk` is the code-pair stride of the
-  // operand layout (PERK for quantized keys, 1 for fp16 keys).
-  auto build_b = [&](const unsigned* sz, int slots, int pk, float kbias) {
-    constexpr int COMBOS = 4 * KS;                 // (gq, ks) per row
-    // threads per (slot, row): as many as keep all 256 busy, a power of two
-    int tpr = NT / (slots * RP);
-    tpr = tpr >= COMBOS ? COMBOS : tpr >= 16 ? 16 : tpr >= 8 ? 8 : tpr >= 4 ? 4
-          : tpr >= 2 ? 2 : 1;
-    const int cpt = COMBOS / tpr;                  // combos per thread
-    for (int it = tid / tpr; it < slots * RP; it += NT / tpr) {
-      const int slot = it / RP, row = it % RP, part = tid % tpr;
-      const float* qr = s_qc + row * D;
-      const unsigned* zs = sz ? sz + slot * D : nullptr;
-      float sum_q = 0.f, sum_z = 0.f;
-      for (int cc = 0; cc < cpt; ++cc) {
-        const int combo = part * cpt + cc;
-        const int cg = combo / KS, ks = combo % KS;
-        unsigned hi4[4], lo4[4];
+  // ---- the stream's run of units (32-bit: L_max <= 2^24 tokens)
+  const int nqt = (int)(a.n_q / kTile), nrt = (int)cdiv(a.n_r, kTile);
+  const int nres = 2 * nrt;                      // ring units
+  const int U = nres + (nqt + C::TPU - 1) / C::TPU;
+  const int64_t Wt = (int64_t)S * NS;
+  auto bound = [&](int64_t x) __attribute__((always_inline)) {
+    int v = (int)(x * U / Wt);
+    if (v < nres && (v & 1)) ++v;                // keep K/V pairs whole
+    return v;
+  };
+  const int64_t c0s = (int64_t)split * NS;
+  const int u0 = bound(c0s + strm), u1 = bound(c0s + strm + 1);
+
+  unsigned char* stages = smem + strm * ST * C::STAGE;
+  const unsigned lds_stages = (unsigned)(uintptr_t)stages;
+  __half* s_q = (__half*)(smem + NS * ST * C::STAGE);
+
+  const uint8_t* kh_base = a.p.k_hi + blk * g.k_block_bytes;
+  const uint8_t* kl_base = C::TWO ? a.p.k_lo + blk * g.k_block_bytes : nullptr;
+  const uint8_t* vh_base = a.p.v_hi + blk * g.v_block_bytes;
+  const uint8_t* vl_base = C::TWO ? a.p.v_lo + blk * g.v_block_bytes : nullptr;
+  const uint8_t* vsz_base = (const uint8_t*)(a.p.v_sz + blk * g.vsz_block);
+  const uint8_t* ksz_base = (const uint8_t*)(a.p.k_sz + blk * g.ksz_block);
+  const uint8_t* kres_base = (const uint8_t*)(a.p.k_res + blk * g.res_block);
+  const uint8_t* vres_base = (const uint8_t*)(a.p.v_res + blk * g.res_block);
+  const int nq_mod = (int)(a.n_q % g.ring);
+  const int tiles_per_group = g.G / kTile;
+
+  auto issue = [&](int u, int slot) __attribute__((always_inline)) {
+    u = __builtin_amdgcn_readfirstlane(u);          // keep the address math scalar
+    const unsigned ld = lds_stages + slot * C::STAGE;
+    if (u < nres) {
+      int slot0 = nq_mod + kTile * (u >> 1);
+      slot0 = slot0 >= g.ring ? slot0 - g.ring : slot0;
+      const uint8_t* src = ((u & 1) ? vres_base : kres_base) + (unsigned)slot0 * (D * 2);
+      dma<C::RESU>(src, ld, lane16);
+    } else {
+      const int t0 = (u - nres) * C::TPU;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int p = 4 * ks + j;
-          int ca, cb;
-          if (sz) {
-            ca = cg * (D / 4) + (p / pk) * 2 * pk + p % pk;
-            cb = ca + pk;
-          } else {
-            ca = cg * (D / 4) + 2 * p;
-            cb = ca + 1;
-          }
-          float xa = qr[ca], xb = qr[cb];
-          if (sz) {
-            const unsigned pa = zs[ca], pb = zs[cb];
-            sum_z += xa * h_hi(pa) + xb * h_hi(pb);
-            xa *= h_lo(pa);
-            xb *= h_lo(pb);
-          }
-          xa = opaque(xa);
-          xb = opaque(xb);
-          const unsigned h = pack2(xa, xb);
-          const unsigned l = pack2(xa - h_lo(h), xb - h_hi(h));
-          hi4[j] = h;
-          lo4[j] = l;
-          sum_q += (h_lo(h) + h_hi(h)) + (h_lo(l) + h_hi(l));
+      for (int j = 0; j < C::TPU; ++j) {
+        const int t = t0 + j;
+        if (t < nqt) {
+          const unsigned lt = ld + j * C::TILE;
+          const unsigned po = (unsigned)t * C::PL;
+          dma<C::PL>(kh_base + po, lt + C::O_KH, lane16);
+          if constexpr (C::TWO) dma<C::PL>(kl_base + po, lt + C::O_KL, lane16);
+          dma<C::PL>(vh_base + po, lt + C::O_VH, lane16);
+          if constexpr (C::TWO) dma<C::PL>(vl_base + po, lt + C::O_VL, lane16);
+          dma<C::VSZB>(vsz_base + (unsigned)t * C::VSZB, lt + C::O_VSZ, lane16);
+          dma<C::KSZB>(ksz_base + (unsigned)(t / tiles_per_group) * C::KSZB,
+                       lt + C::O_KSZ, lane16);
         }
-        u4v* dst = s_bq + ((slot * NRT + row / 16) * KS + ks) * 128 + 16 * cg + row % 16;
-        dst[0] = u4v{hi4[0], hi4[1], hi4[2], hi4[3]};
-        dst[64] = u4v{lo4[0], lo4[1], lo4[2], lo4[3]};
       }
-      for (int o = 1; o < tpr; o <<= 1) {
-        sum_q += __shfl_xor(sum_q, o);
-        sum_z += __shfl_xor(sum_z, o);
-      }
-      if (part == 0) s_bias[slot * RP + row] = sum_z - kbias * sum_q;
     }
   };
+  auto count = [&](int u) __attribute__((always_inline)) -> int {
+    if (u < nres) return C::NIR;
+    const int left = nqt - (u - nres) * C::TPU;
+    return (left < C::TPU ? left : C::TPU) * C::NI_TILE;
+  };
 
-  float m_run[NRT], l_run[NRT];
-  f4v acc[NRT][MT];
-  float zacc[NRT][NG];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) zacc[rt][gg] = 0.f;
+  // ---- stage the query rows and prefetch the first ST-1 units.  The rows
+  // come in with the same direct copies (16-byte chunk k of s_q from row
+  // k / (D/8)); copy instruction i is issued by wave i % NW before its units,
+  // so waiting for its units' count leaves the query rows landed.
+  const int q_chunks = a.rows * (D / 8);
+  int my_q = 0;
+  for (int i = wave; i * kWave < q_chunks; i += C::NW) {
+    const int k = i * kWave + lane;
+    const unsigned ldq = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)s_q + 16u * i * kWave);
+    if (k < q_chunks) {
+      const int r = k / (D / 8), c8 = k % (D / 8);
+      const int t = r / a.gs, hl = r % a.gs;
+      const unsigned off = (unsigned)((((int64_t)b * a.T + t) * a.Hq +
+                                       kvh * a.gs + hl) * D + 8 * c8) * 2u;
+      dma16(a.q, off, ldq);
+    }
+    ++my_q;
   }
-  const bool residual = split >= a.s_q;
-  float oscale = 1.f;
+  // Only the first unit goes out with the query rows: the whole grid's
+  // first requests then land sooner, the rest of the prefetch follows once
+  // the rows are in.
+  int slot_in = 0, pro = 0;
+  if (loader && u0 < u1) {
+    issue(u0, slot_in);
+    pro = count(u0);
+    slot_in = 1;
+  }
+  for (int k = q_chunks + tid; k < RP * (D / 8); k += NT)   // padded rows
+    *(uint4*)(s_q + 8 * k) = make_uint4(0u, 0u, 0u, 0u);
+  if (my_q) wait_le<C::NIQ, C::NIR, 1>(pro);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (loader) {
+    for (int u = u0 + 1; u < u0 + ST - 1 && u < u1; ++u) {
+      issue(u, slot_in);
+      slot_in = slot_in + 1 == ST ? 0 : slot_in + 1;
+    }
+  }
 
-  // Online-softmax update of row tile rt from the S^T accumulators of the
-  // two subtiles; returns the probabilities in place.
-  // The probabilities come out scaled by 2^pexp (the exponent is shifted
-  // by pexp), so l and the zero-point sums carry that factor too; it is
-  // removed once per wave at the end.
-  auto softmax_update = [&](int rt, f4v& s0, f4v& s1, float pexp) {
-    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-    mx = xor_max(mx, a16, a32);
-    const float mnew = fmaxf(m_run[rt], mx);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = fast_exp2(m_run[rt] - mref);
-    const float mshift = mref - pexp;
+  // ---- per-wave state (one 16-row tile)
+  float m_ref = -INFINITY, sig = 0.f, l_run = 0.f, binit = 0.f;
+  f4v cinit = f4v{0.f, 0.f, 0.f, 0.f};
+  f4v acc[MT];
+  float zacc[NG];
+  u4v bqh[KS], bql[KS];                // B operands Q' = hi + lo
+  u4v bpres = u4v{0u, 0u, 0u, 0u};     // ring tile: P' between its two units
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s0[i] = fast_exp2(s0[i] - mshift);
-      s1[i] = fast_exp2(s1[i] - mshift);
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) zacc[gg] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) bqh[ks] = bql[ks] = u4v{0u, 0u, 0u, 0u};
+  int cur_grp = -2;                    // -1: ring operands, >= 0: key group
+  const DecK dk = dec_consts();
+  const float c0 = a.c0;
+  const __half* qrow = s_q + row * D;
+  // q * c0 of the channels this lane multiplies in key-group operands:
+  // (cA(ks) + j, cB(ks) + j), fixed for the whole run
+  auto chan_a = [&](int ks) __attribute__((always_inline)) {
+    if constexpr (C::W == 4) return gq * (D / 4) + 8 * ks;
+    else if constexpr (C::W == 2) return gq * (D / 4) + 16 * (ks / 2) + 4 * (ks % 2);
+    else return gq * (D / 4) + 4 * ks;
+  };
+  constexpr int DAB = C::W == 4 ? 4 : C::W == 2 ? 8 : 16;   // cB - cA
+  float qcA[KS][4], qcB[KS][4];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u2v qa = *(const u2v*)(qrow + chan_a(ks));
+    const u2v qb = *(const u2v*)(qrow + chan_a(ks) + DAB);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qcA[ks][j] = h_at(qa, j) * c0;
+      qcB[ks][j] = h_at(qb, j) * c0;
     }
-    const float ps = ((s0[0] + s1[0]) + (s0[1] + s1[1])) +
-                     ((s0[2] + s1[2]) + (s0[3] + s1[3]));
-    l_run[rt] = l_run[rt] * alpha + ps;
-    m_run[rt] = mnew;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[rt][mt] *= alpha;
-#pragma unroll
-      for (int gg = 0; gg < NG; ++gg) zacc[rt][gg] *= alpha;
-    }
+  }
+
+  auto refresh = [&]() __attribute__((always_inline)) {
+    const float v = binit + sig;
+    cinit = f4v{v, v, v, v};
   };
 
-  // S^T = K Q'^T for the two 16-token subtiles, B operands from LDS slot.
-  auto scores = [&](f4v (&sc)[2][NRT], const u4v (&ak)[2][KS], int slot) {
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const float bias = s_bias[slot * RP + l16 + 16 * rt];
-      sc[0][rt] = f4v{bias, bias, bias, bias};
-      sc[1][rt] = sc[0][rt];
-    }
+  // B operands of the fp16 ring: q * c0 over natural channel pairs
+  // (2j, 2j+1) of each 8-channel k-step slice.
+  auto build_res = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      const u4v q8 = *(const u4v*)(qrow + gq * (D / 4) + 8 * ks);
+      unsigned hi[4], lo[4];
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const u4v* src = s_bq + ((slot * NRT + rt) * KS + ks) * 128 + lane;
-        const u4v bh = src[0], bl = src[64];
+      for (int j = 0; j < 4; ++j) {
+        const float xa = opaque(h_lo(q8[j]) * c0);
+        const float xb = opaque(h_hi(q8[j]) * c0);
+        hi[j] = pack2(xa, xb);
+        lo[j] = pack2(xa - h_lo(hi[j]), xb - h_hi(hi[j]));
+      }
+      bqh[ks] = u4v{hi[0], hi[1], hi[2], hi[3]};
+      bql[ks] = u4v{lo[0], lo[1], lo[2], lo[3]};
+    }
+    binit = 0.f;
+    refresh();
+  };
+
+  // B operands of one key group: Q' = q * c0 * s over the channel pairs the
+  // code decoder produces for k-step ks: (cA + j, cB + j), j = 0..3; the
+  // accumulator start is  sum_c q c0 z - KBIAS * sum_c Q'  (the second sum
+  // by MFMA against a constant operand, over the same fp16 parts).
+  auto build_quant = [&](const unsigned char* ksz) __attribute__((always_inline)) {
+    float zs = 0.f;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          sc[st][rt] = mfma16(ak[st][ks], bh, sc[st][rt]);
-          sc[st][rt] = mfma16(ak[st][ks], bl, sc[st][rt]);
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cA = chan_a(ks);
+      const u4v sA = *(const u4v*)(ksz + 4 * cA);          // {s, z} of cA .. cA+3
+      const u4v sB = *(const u4v*)(ksz + 4 * (cA + DAB));
+      unsigned hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // fma with +0 keeps the fp16 operand unconverted (mixed fma)
+        const float xa = opaque(__builtin_fmaf(qcA[ks][j], h_lo(sA[j]), 0.f));
+        const float xb = opaque(__builtin_fmaf(qcB[ks][j], h_lo(sB[j]), 0.f));
+        hi[j] = pack2(xa, xb);
+        lo[j] = pack2(__builtin_fmaf(h_lo(hi[j]), -1.f, xa),
+                      __builtin_fmaf(h_hi(hi[j]), -1.f, xb));
+        zs = __builtin_fmaf(qcA[ks][j], h_hi(sA[j]), zs);
+        zs = __builtin_fmaf(qcB[ks][j], h_hi(sB[j]), zs);
+      }
+      bqh[ks] = u4v{hi[0], hi[1], hi[2], hi[3]};
+      bql[ks] = u4v{lo[0], lo[1], lo[2], lo[3]};
+    }
+    const float z = sum_x4(zs);
+    f4v cc = f4v{z, z, z, z};
+    if constexpr (C::KBIAS != 0.f) {
+      const u4v kn = u4v{C::NEG, C::NEG, C::NEG, C::NEG};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        cc = mfma16(kn, bqh[ks], cc);
+        cc = mfma16(kn, bql[ks], cc);
       }
     }
+    binit = cc[0];
+    refresh();
   };
 
-  // Key scale/zero of groups [g0, g0 + slots) for the round starting at
-  // tile tr: this thread's share of the ngr * D u32, loaded to registers
-  // now and stored to LDS buffer `buf` later (after the round's compute).
-  constexpr int KSZ_PER = 2;   // u32 per thread: ngr * D <= 512
-  auto ksz_fetch = [&](const __half2* base, int64_t g0, int slots, unsigned* r) {
+  // S^T = K Q'^T for the two 16-token subtiles, started at cinit.
+  auto scores = [&](f4v (&sc)[2], const u4v (&ak)[2][KS]) {
+    sc[0] = sc[1] = cinit;
 #pragma unroll
-    for (int k = 0; k < KSZ_PER; ++k) {
-      const int e = tid + k * NT;
-      r[k] = e < slots * D ? ((const unsigned*)(base + g0 * D))[e] : 0u;
-    }
-  };
-  auto ksz_park = [&](int buf, const unsigned* r) {
-#pragma unroll
-    for (int k = 0; k < KSZ_PER; ++k) {
-      const int e = tid + k * NT;
-      if (e < ngr * D) s_ksz[buf * ngr * D + e] = r[k];
-    }
-  };
-
-  if (!residual) {
-    // ================= quantized prefix ===================================
-    oscale = 1.f / kPScale;
-    const int64_t nqt = a.n_q / kTile;
-    const int64_t T0 = (int64_t)split * NW * a.tpw;
-    const int64_t T1 = T0 + (int64_t)NW * a.tpw < nqt ? T0 + (int64_t)NW * a.tpw : nqt;
-    const uint8_t* kh_base = a.p.k_hi + blk * g.k_block_bytes;
-    const uint8_t* kl_base = C::TWO ? a.p.k_lo + blk * g.k_block_bytes : nullptr;
-    const uint8_t* vh_base = a.p.v_hi + blk * g.v_block_bytes;
-    const uint8_t* vl_base = C::TWO ? a.p.v_lo + blk * g.v_block_bytes : nullptr;
-    const __half2* vsz_base = a.p.v_sz + blk * g.vsz_block;
-    const __half2* ksz_base = a.p.k_sz + blk * g.ksz_block;
-    const int64_t krow = D * C::W / 8;
-    const int kofs = gq * (D * C::W / 32);
-    const int vofs = lane * (D * C::W / 16);
-    const int64_t ngroups = a.n_q / g.G;
-
-    // Load pointers of one tile for this lane; next() moves them NW tiles on.
-    struct TP {
-      const uint8_t *kh, *kl, *vh, *vl;
-      const unsigned *s;
-    };
-    const int64_t kstep = (int64_t)kTile * krow;       // bytes per K tile
-    auto tile_ptr = [&](int64_t t) {
-      TP p;
-      p.kh = kh_base + (t * kTile + l16) * krow + kofs;
-      p.kl = C::TWO ? kl_base + (t * kTile + l16) * krow + kofs : nullptr;
-      p.vh = vh_base + t * g.v_tile_bytes + vofs;
-      p.vl = C::TWO ? vl_base + t * g.v_tile_bytes + vofs : nullptr;
-      p.s = (const unsigned*)(vsz_base + t * g.vsz_tile) + gq * 4 * NG;
-      return p;
-    };
-    auto next = [&](TP& p) {
-      p.kh += NW * kstep;
-      if constexpr (C::TWO) p.kl += NW * kstep;
-      p.vh += NW * g.v_tile_bytes;
-      if constexpr (C::TWO) p.vl += NW * g.v_tile_bytes;
-      p.s += NW * g.vsz_tile;
-    };
-    auto load_tile = [&](QTile<C>& tl, const TP& p) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        ldg<C::NDK>(p.kh + st * 16 * krow, tl.kh[st]);
-        if constexpr (C::TWO) ldg<C::NDK>(p.kl + st * 16 * krow, tl.kl[st]);
+        sc[st] = mfma16(ak[st][ks], bqh[ks], sc[st]);
+        sc[st] = mfma16(ak[st][ks], bql[ks], sc[st]);
       }
-      ldg<C::NDV>(p.vh, tl.vh);
-      if constexpr (C::TWO) ldg<C::NDV>(p.vl, tl.vl);
-      ldg<4 * NG>(p.s, tl.sz);                     // scale pairs
-      ldg<4 * NG>(p.s + 16 * NG, tl.sz + 4 * NG);  // zero-point pairs
-    };
+  };
 
-    const DecK dk = dec_consts();
-    auto compute_tile = [&](const QTile<C>& tl, int slot) {
-      // ---- K operands: codes (or draft points) as fp16, both subtiles
-      u4v ak[2][KS];
+  // Online softmax over the 8 scores this lane holds (taken relative to the
+  // row reference, + kPExp); returns p' in place.  Fast path: every score
+  // of the wave is within kTau of its row reference.
+  auto softmax = [&](f4v& s0, f4v& s1) __attribute__((always_inline)) {
+    const float lm = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                           fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    const bool fin = m_ref != -INFINITY;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(fin && lm <= kPExp + kTau)) == 0, 1)) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          unsigned r[4];
-          if constexpr (PATH == P_T8) {
-            dec8(tl.kh[st][ks], tl.kl[st][ks], r, dk);
-          } else if constexpr (PATH == P_D4) {
-            dec4(tl.kh[st][ks], r, dk);
-          } else {
-            constexpr int KPD = C::PERK / 4;   // k-steps per dword
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              r[j] = declow<C::W>(tl.kh[st][ks / KPD], 4 * (ks % KPD) + j, dk);
-          }
-          ak[st][ks] = u4v{r[0], r[1], r[2], r[3]};
-        }
-      f4v sc[2][NRT];
-      scores(sc, ak, slot);
-      // ---- softmax and P' = p * s_v * 2^10 for every row tile
-      u4v bp[NRT][NG];
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        softmax_update(rt, sc[0][rt], sc[1][rt], kPExp);
-        // P' pair i (tokens 4gq+i, 16+4gq+i) = fp16(p) * scale pair
-        unsigned pp[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pp[i] = pack2(sc[0][rt][i], sc[1][rt][i]);
-#pragma unroll
-        for (int gg = 0; gg < NG; ++gg) {
-          float zs = zacc[rt][gg];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const unsigned sp = tl.sz[i * NG + gg];            // scales
-            const unsigned zp = tl.sz[(4 + i) * NG + gg];      // zero-points
-            bp[rt][gg][i] = __builtin_bit_cast(
-                unsigned, __builtin_bit_cast(h2v, pp[i]) * __builtin_bit_cast(h2v, sp));
-            zs += sc[0][rt][i] * h_lo(zp);
-            zs += sc[1][rt][i] * h_hi(zp);
-          }
-          zacc[rt][gg] = zs;
-        }
+      for (int i = 0; i < 4; ++i) {
+        s0[i] = fast_exp2(s0[i]);
+        s1[i] = fast_exp2(s1[i]);
       }
-      // ---- O^T += V^T P'^T, one 16-channel tile of exact codes at a time
+    } else {
+      const float mx = max_x4(lm);               // row max, shifted
+      const bool trig = !fin || mx > kPExp + kTau;
+      const float m_old = m_ref;
+      const float m_new = trig ? fmaxf(m_old, mx - sig) : m_old;
+      const float mref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_old - mref);   // 0 when m_old = -inf
+      const float delta = sig + mref - kPExp;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int i = 0; i < 4; ++i) {
+        s0[i] = fast_exp2(s0[i] - delta);
+        s1[i] = fast_exp2(s1[i] - delta);
+      }
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        l_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) zacc[gg] *= alpha;
+      }
+      m_ref = m_new;
+      sig = m_new == -INFINITY ? 0.f : kPExp - m_new;
+      refresh();
+    }
+    l_run += ((s0[0] + s1[0]) + (s0[1] + s1[1])) +
+             ((s0[2] + s1[2]) + (s0[3] + s1[3]));
+  };
+
+  // ---- one quantized 32-token tile from LDS
+  auto quant_tile = [&](const unsigned char* tb, int t, bool may_build)
+      __attribute__((always_inline)) {
+    const int grp = t / tiles_per_group;
+    if (may_build && grp != cur_grp) {
+      build_quant(tb + C::O_KSZ);
+      cur_grp = grp;
+    }
+    u4v ak[2][KS];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int ko = (l16 + 16 * st) * (D * C::W / 8) + gq * (D * C::W / 32);
+      unsigned kh[C::NDK], kl[C::TWO ? C::NDK : 1];
+      lds_read<C::NDK>(tb + C::O_KH + ko, kh);
+      if constexpr (C::TWO) lds_read<C::NDK>(tb + C::O_KL + ko, kl);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
         unsigned r[4];
         if constexpr (PATH == P_T8) {
-          dec8(tl.vh[mt], tl.vl[mt], r, dk);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) r[j] = hadd2(r[j], kMinus1024);
+          dec8(kh[ks], kl[ks], r, dk);
         } else if constexpr (PATH == P_D4) {
-          dec4(tl.vh[mt], r, dk);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) r[j] = hadd2(r[j], kMinusDraft);
+          dec4(kh[ks], r, dk);
         } else {
-          constexpr int PER = 4 / C::W;   // channel tiles per dword
+          constexpr int KPD = 16 / C::W / 4;   // k-steps per dword
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            r[j] = declow<C::W>(tl.vh[mt / PER], 4 * (mt % PER) + j, dk);
+            r[j] = declow<C::W>(kh[ks / KPD], 4 * (ks % KPD) + j, dk);
         }
-        const u4v av = u4v{r[0], r[1], r[2], r[3]};
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-          acc[rt][mt] = mfma16(av, bp[rt][mt / (MT / NG)], acc[rt][mt]);
-      }
-    };
-
-    // Rounds of NW consecutive tiles, wave w on the w-th: the round's key
-    // groups are built once for the workgroup.  Every wave runs every round
-    // (and its barriers); the next round's tile is prefetched before the
-    // current one is computed.
-    auto slots_of = [&](int64_t g0) {
-      return g0 + ngr > ngroups ? (int)(ngroups - g0) : ngr;
-    };
-    // Rounds of NW consecutive tiles, wave w on the w-th.  The groups a
-    // round needs are built into B operands once for the workgroup (between
-    // two barriers) from scales parked in LDS by the previous round, whose
-    // loads were in flight during its compute.
-    int64_t cur_g0 = -1, parked_g0 = -1;
-    int buf = 0;
-    unsigned kpre[KSZ_PER];
-    TP np = tile_ptr(T0 + wave);          // next tile to load
-    auto round = [&](int64_t tr, QTile<C>& cur, QTile<C>& nxt) {
-      const int64_t t = tr + wave;
-      const int64_t g0 = tr * kTile / g.G;
-      if (g0 != cur_g0) {
-        __syncthreads();                       // old B operands consumed,
-        build_b(s_ksz + buf * ngr * D,         // parked scales visible
-                slots_of(g0), C::PERK, C::KBIAS);
-        __syncthreads();
-        cur_g0 = g0;
-      }
-      if (t + NW < T1) {
-        load_tile(nxt, np);
-        next(np);
-      }
-      const int64_t gn = (tr + NW) * kTile / g.G;   // next round's groups
-      const bool fetch = tr + NW < T1 && gn != g0 && gn != parked_g0;
-      if (fetch) ksz_fetch(ksz_base, gn, slots_of(gn), kpre);
-      if (t < T1) compute_tile(cur, (int)(t * kTile / g.G - g0));
-      if (fetch) {
-        buf ^= 1;
-        ksz_park(buf, kpre);
-        parked_g0 = gn;
-      }
-    };
-    if (T0 < T1) {
-      QTile<C> ta, tb;
-      if (T0 + wave < T1) {
-        load_tile(ta, np);
-        next(np);
-      }
-      const int64_t g_first = T0 * kTile / g.G;
-      ksz_fetch(ksz_base, g_first, slots_of(g_first), kpre);
-  // ---- q * c0 of this block's rows (row = t * gs + head-in-group) as fp32 in
-    // LDS: 16-byte loads, all issued before the first LDS store
-    {
-      constexpr int CH = RP * D / 8;                 // 8-half chunks
-      constexpr int PER = (CH + NT - 1) / NT;
-      uint4 v[PER];
-  #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int e = tid + k * NT;
-        const int row = e / (D / 8), c8 = e % (D / 8);
-        v[k] = make_uint4(0u, 0u, 0u, 0u);
-        if (e < CH && row < a.rows) {
-          const int t = row / a.gs, hl = row % a.gs;
-          v[k] = *(const uint4*)(a.q + (((int64_t)b * a.T + t) * a.Hq +
-                                        kvh * a.gs + hl) * D + 8 * c8);
-        }
-      }
-  #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int e = tid + k * NT;
-        if (e < CH) {
-          const unsigned w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-          f4v lo4, hi4;
-  #pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            lo4[2 * x] = h_lo(w4[x]) * a.c0;
-            lo4[2 * x + 1] = h_hi(w4[x]) * a.c0;
-            hi4[2 * x] = h_lo(w4[2 + x]) * a.c0;
-            hi4[2 * x + 1] = h_hi(w4[2 + x]) * a.c0;
-          }
-          *(f4v*)(s_qc + 8 * e) = lo4;
-          *(f4v*)(s_qc + 8 * e + 4) = hi4;
-        }
+        ak[st][ks] = u4v{r[0], r[1], r[2], r[3]};
       }
     }
-    __syncthreads();
-      ksz_park(buf, kpre);
-      parked_g0 = g_first;
-      __syncthreads();
-      for (int64_t tr = T0; tr < T1; tr += 2 * NW) {
-        round(tr, ta, tb);
-        if (tr + NW < T1) round(tr + NW, tb, ta);
+    f4v sc[2];
+    scores(sc, ak);
+    softmax(sc[0], sc[1]);
+    // value scale pairs (tokens 4gq+i, 16+4gq+i; [i][group]) and zero pairs
+    unsigned sz[8 * NG];
+    lds_read<4 * NG>(tb + C::O_VSZ + 16 * NG * gq, sz);
+    lds_read<4 * NG>(tb + C::O_VSZ + 16 * NG * gq + 64 * NG, sz + 4 * NG);
+    unsigned pp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pp[i] = pack2(sc[0][i], sc[1][i]);
+    u4v bp[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      float z = zacc[gg];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned q = hmul2(pp[i], sz[i * NG + gg]);
+        bp[gg][i] = q;
+        z = dot2(pp[i], sz[4 * NG + i * NG + gg], z);
+        if constexpr (!C::LOW) z = dot2(q, C::NEG, z);   // code offset
+      }
+      zacc[gg] = z;
+    }
+    unsigned vh[C::NDV], vl[C::TWO ? C::NDV : 1];
+    lds_read<C::NDV>(tb + C::O_VH + lane * (D * C::W / 16), vh);
+    if constexpr (C::TWO) lds_read<C::NDV>(tb + C::O_VL + lane * (D * C::W / 16), vl);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      unsigned r[4];
+      if constexpr (PATH == P_T8) {
+        dec8(vh[mt], vl[mt], r, dk);
+      } else if constexpr (PATH == P_D4) {
+        dec4(vh[mt], r, dk);
+      } else {
+        constexpr int PER = 4 / C::W;   // channel tiles per dword
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          r[j] = declow<C::W>(vh[mt / PER], 4 * (mt % PER) + j, dk);
+      }
+      acc[mt] = mfma16(u4v{r[0], r[1], r[2], r[3]}, bp[mt / (MT / NG)], acc[mt]);
+    }
+  };
+
+  // ---- ring tile r, first unit: fp16 K -> scores, mask, softmax, P'
+  auto ring_k = [&](const unsigned char* sb, int r) __attribute__((always_inline)) {
+    if (cur_grp != -1) {
+      build_res();
+      cur_grp = -1;
+    }
+    u4v ak[2][KS];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      unsigned kd[D / 8];
+      lds_read<D / 8>(sb + ((l16 + 16 * st) * D + gq * (D / 4)) * 2, kd);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ak[st][ks] = u4v{kd[4 * ks], kd[4 * ks + 1], kd[4 * ks + 2], kd[4 * ks + 3]};
+    }
+    f4v sc[2];
+    scores(sc, ak);
+    // causal / validity mask: row sees positions <= L - T + t(row)
+    const int p0 = (int)a.n_q + kTile * r;
+    const int lim = row < a.rows ? L - a.T + row / a.gs : L - 1;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = p0 + 16 * st + 4 * gq + i;
+        sc[st][i] = pos <= lim ? sc[st][i] : -INFINITY;
+      }
+    softmax(sc[0], sc[1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bpres[i] = pack2(sc[0][i], sc[1][i]);
+  };
+
+  // ---- ring tile r, second unit: fp16 V (token-permuted) -> O
+  auto ring_v = [&](const unsigned char* sb, int r) __attribute__((always_inline)) {
+    unsigned vd[D / 4];
+    lds_read<D / 4>(sb + lane * D, vd);
+    const int p0 = (int)a.n_q + kTile * r;
+    if (p0 + kTile > L) {              // zero the slots past the context
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned keep = (p0 + 4 * gq + i < L ? 0x0000FFFFu : 0u) |
+                              (p0 + 16 + 4 * gq + i < L ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) vd[4 * mt + i] &= keep;
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      acc[mt] = mfma16(
+          u4v{vd[4 * mt], vd[4 * mt + 1], vd[4 * mt + 2], vd[4 * mt + 3]},
+          bpres, acc[mt]);
+  };
+
+  // ---- the unit loops, ring tiles first (K and V unit pairs), then the
+  // quantized prefix
+  int slot = 0;
+  auto next_slot = [](int x) __attribute__((always_inline)) { return x + 1 == ST ? 0 : x + 1; };
+  // may_build = false when every tile of the unit is known to belong to
+  // the current key group: the inner loops below then carry the B operands
+  // unchanged, so they stay in place in registers.
+  auto quant_unit = [&](int u, bool may_build) __attribute__((always_inline)) {
+    const unsigned char* sb = stages + slot * C::STAGE;
+    const int t0 = (u - nres) * C::TPU;
+#pragma unroll
+    for (int j = 0; j < C::TPU; ++j)
+      if (t0 + j < nqt) quant_tile(sb + j * C::TILE, t0 + j, may_build);
+  };
+  auto in_group = [&](int u) __attribute__((always_inline)) {
+    const int t0 = (u - nres) * C::TPU;
+    const int t1 = (t0 + C::TPU < nqt ? t0 + C::TPU : nqt) - 1;
+    return t0 / tiles_per_group == cur_grp && t1 / tiles_per_group == cur_grp;
+  };
+  if constexpr (!PAIR) {
+    // issue unit u + ST - 1 (into the slot of unit u - 1, computed by this
+    // wave), wait until unit u has landed, compute it
+    auto step = [&](int u) __attribute__((always_inline)) {
+      if (u + ST - 1 < u1) {
+        issue(u + ST - 1, slot_in);
+        slot_in = next_slot(slot_in);
+      }
+      int pending = 0;
+#pragma unroll
+      for (int k = 1; k < ST; ++k)
+        if (u + k < u1) pending += count(u + k);
+      wait_le<C::NIQ, C::NIR, ST - 1>(pending);
+    };
+    int u = u0;
+    const int ur = u1 < nres ? u1 : nres;
+    for (; u < ur; u += 2) {
+      step(u);
+      ring_k(stages + slot * C::STAGE, u >> 1);
+      slot = next_slot(slot);
+      step(u + 1);
+      ring_v(stages + slot * C::STAGE, u >> 1);
+      slot = next_slot(slot);
+    }
+    while (u < u1) {
+      step(u);
+      quant_unit(u, true);
+      slot = next_slot(slot);
+      ++u;
+      for (; u < u1 && in_group(u); ++u) {
+        step(u);
+        quant_unit(u, false);
+        slot = next_slot(slot);
       }
     }
   } else {
-    // ================= fp16 residual ring ==================================
-  // ---- q * c0 of this block's rows (row = t * gs + head-in-group) as fp32 in
-    // LDS: 16-byte loads, all issued before the first LDS store
-    {
-      constexpr int CH = RP * D / 8;                 // 8-half chunks
-      constexpr int PER = (CH + NT - 1) / NT;
-      uint4 v[PER];
-  #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int e = tid + k * NT;
-        const int row = e / (D / 8), c8 = e % (D / 8);
-        v[k] = make_uint4(0u, 0u, 0u, 0u);
-        if (e < CH && row < a.rows) {
-          const int t = row / a.gs, hl = row % a.gs;
-          v[k] = *(const uint4*)(a.q + (((int64_t)b * a.T + t) * a.Hq +
-                                        kvh * a.gs + hl) * D + 8 * c8);
-        }
+    // Two waves read every stage.  Per unit: the loader waits until unit u
+    // has landed, a workgroup barrier shows it to the partner and proves
+    // both are done with unit u - 1, then the loader refills that slot with
+    // unit u + ST - 1.  Every wave of the workgroup runs the same number of
+    // barriers: each phase iterates to the longest stream's count.
+    int n_ring = 0, n_quant = 0;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int a0 = bound(c0s + k), a1 = bound(c0s + k + 1);
+      const int r1 = a1 < nres ? a1 : nres;
+      const int nr = r1 > a0 ? r1 - a0 : 0;
+      const int q0 = a0 > nres ? a0 : nres;
+      const int nq = a1 > q0 ? a1 - q0 : 0;
+      n_ring = nr > n_ring ? nr : n_ring;
+      n_quant = nq > n_quant ? nq : n_quant;
+    }
+    auto sync_step = [&](int u, bool active) __attribute__((always_inline)) {
+      if (loader && active) {
+        int pending = 0;
+#pragma unroll
+        for (int k = 1; k + 1 < ST; ++k)
+          if (u + k < u1) pending += count(u + k);
+        wait_le<C::NIQ, C::NIR, ST - 2>(pending);
       }
-  #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int e = tid + k * NT;
-        if (e < CH) {
-          const unsigned w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-          f4v lo4, hi4;
-  #pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            lo4[2 * x] = h_lo(w4[x]) * a.c0;
-            lo4[2 * x + 1] = h_hi(w4[x]) * a.c0;
-            hi4[2 * x] = h_lo(w4[2 + x]) * a.c0;
-            hi4[2 * x + 1] = h_hi(w4[2 + x]) * a.c0;
-          }
-          *(f4v*)(s_qc + 8 * e) = lo4;
-          *(f4v*)(s_qc + 8 * e + 4) = hi4;
-        }
+      // plain s_barrier (a __syncthreads fence would also wait for every
+      // copy in flight); the asm statements keep LDS accesses on their side
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (loader && active && u + ST - 1 < u1) {
+        issue(u + ST - 1, slot_in);
+        slot_in = next_slot(slot_in);
+      }
+    };
+    const int ur = u1 < nres ? u1 : nres;
+    for (int i = 0; i < n_ring; i += 2) {
+      const int u = u0 + i;
+      const bool active = u < ur;
+      sync_step(u, active);
+      if (active) {
+        ring_k(stages + slot * C::STAGE, u >> 1);
+        slot = next_slot(slot);
+      }
+      sync_step(u + 1, active);
+      if (active) {
+        ring_v(stages + slot * C::STAGE, u >> 1);
+        slot = next_slot(slot);
       }
     }
-    __syncthreads();
-    build_b(nullptr, 1, 1, 0.f);   // q * c0 = hi + lo, natural channel pairs
-    __syncthreads();
-    const int64_t ti = (int64_t)(split - a.s_q) * NW + wave;
-    const int64_t nrt = cdiv(a.n_r, kTile);
-    if (ti < nrt) {
-      const int64_t p0 = a.n_q + ti * kTile;           // first position
-      const int64_t slot0 = p0 % g.ring;               // 32-aligned slot
-      const __half* kres = a.p.k_res + blk * g.res_block;
-      u4v ak[2][KS];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        unsigned kd[D / 8];
-        ldg<D / 8>(kres + (slot0 + 16 * st + l16) * D + gq * (D / 4), kd);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ak[st][ks] = u4v{kd[4 * ks], kd[4 * ks + 1], kd[4 * ks + 2], kd[4 * ks + 3]};
-      }
-      unsigned vd[D / 4];
-      ldg<D / 4>(a.p.v_res + blk * g.res_block + (slot0 / kTile) * kTile * D +
-                     lane * (D / 2),
-                 vd);
-      f4v sc[2][NRT];
-      scores(sc, ak, 0);
-      // causal / validity mask: row sees positions <= L - T + t(row)
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const int row = l16 + 16 * rt;
-        const int64_t lim = row < a.rows ? L - a.T + row / a.gs : L - 1;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t pos = p0 + 16 * st + 4 * gq + i;
-            sc[st][rt][i] = pos <= lim ? sc[st][rt][i] : -INFINITY;
-          }
-      }
-      // V tile (token-permuted fp16): zero the slots past the context
-      if (p0 + kTile > L) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const unsigned keep =
-              (p0 + 4 * gq + i < L ? 0x0000FFFFu : 0u) |
-              (p0 + 16 + 4 * gq + i < L ? 0xFFFF0000u : 0u);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) vd[4 * mt + i] &= keep;
+    // every iteration, outer or inner, runs exactly one barrier
+    const int uq = u0 > nres ? u0 : nres;
+    int i = 0;
+    while (i < n_quant) {
+      {
+        const int u = uq + i;
+        const bool active = u < u1;
+        sync_step(u, active);
+        if (active) {
+          quant_unit(u, true);
+          slot = next_slot(slot);
         }
+        ++i;
       }
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        softmax_update(rt, sc[0][rt], sc[1][rt], 0.f);
-        u4v bp;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bp[i] = pack2(sc[0][rt][i], sc[1][rt][i]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[rt][mt] = mfma16(
-              u4v{vd[4 * mt], vd[4 * mt + 1], vd[4 * mt + 2], vd[4 * mt + 3]},
-              bp, acc[rt][mt]);
+      for (; i < n_quant; ++i) {
+        const int u = uq + i;
+        const bool active = u < u1;
+        if (active && !in_group(u)) break;
+        sync_step(u, active);
+        if (active) {
+          quant_unit(u, false);
+          slot = next_slot(slot);
+        }
       }
     }
   }
 
-  // ---- per-wave finish: full-row l, zero-point term folded into o; the
-  // quantized waves' sums carry the 2^10 of their probabilities (oscale)
+  // ---- per-wave finish: full-row l, zero-point term folded into o; all
+  // sums carry the 2^kPExp of the probabilities
+  l_run = sum_x4(l_run) * kOScale;
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    l_run[rt] = xor_sum(l_run[rt], a16, a32) * oscale;
+  for (int gg = 0; gg < NG; ++gg) zacc[gg] = sum_x4(zacc[gg]) * kOScale;
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) zacc[rt][gg] = xor_sum(zacc[rt][gg], a16, a32) * oscale;
+  for (int mt = 0; mt < MT; ++mt)
+    acc[mt] = acc[mt] * kOScale + zacc[mt / (MT / NG)];
+
+  // ---- merge the NS streams (per row tile) through LDS, halving each step
+  // slab rows padded by 4 floats: the 16 rows of a put/take land in
+  // different banks
+  constexpr int DP = D + 4;
+  float* s_slab = (float*)smem;
+  float* s_ml = s_slab + (NS / 2) * NH * 16 * DP;
+  auto put = [&](int slot_m) __attribute__((always_inline)) {
+    float* o = s_slab + (slot_m * NH + h) * 16 * DP;
+    float* ml = s_ml + (slot_m * NH + h) * 32;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      acc[rt][mt] = acc[rt][mt] * oscale + zacc[rt][mt / (MT / NG)];
+      *(f4v*)(o + l16 * DP + 16 * mt + 4 * gq) = acc[mt];
+    if (gq == 0) {
+      ml[l16] = m_ref;
+      ml[16 + l16] = l_run;
+    }
+  };
+  auto take = [&](int slot_m) __attribute__((always_inline)) {
+    const float* o = s_slab + (slot_m * NH + h) * 16 * DP;
+    const float* ml = s_ml + (slot_m * NH + h) * 32;
+    const float mo = ml[l16], lo = ml[16 + l16];
+    const float M = fmaxf(m_ref, mo);
+    const float fa = M == -INFINITY ? 0.f : fast_exp2(m_ref - M);
+    const float fb = M == -INFINITY ? 0.f : fast_exp2(mo - M);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      acc[mt] = acc[mt] * fa + *(const f4v*)(o + l16 * DP + 16 * mt + 4 * gq) * fb;
+    l_run = l_run * fa + lo * fb;
+    m_ref = M;
+  };
+  __syncthreads();   // every stream is done with its stages
+#pragma unroll
+  for (int half = NS / 2; half >= 1; half /= 2) {
+    if (strm >= half && strm < 2 * half) put(strm - half);
+    __syncthreads();
+    if (strm < half) take(strm);
+    __syncthreads();
   }
 
-  // ---- merge the 4 waves through LDS: (2,3) -> (0,1), then 1 -> 0
-  float* s_slab = (float*)smem;
-  float* s_ml = s_slab + 2 * RP * D;
-  auto put = [&](int slot) {
-    float* o = s_slab + slot * RP * D;
-    float* ml = s_ml + slot * 2 * RP;
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int row = l16 + 16 * rt;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        *(f4v*)(o + row * D + 16 * mt + 4 * gq) = acc[rt][mt];
-      if (gq == 0) {
-        ml[row] = m_run[rt];
-        ml[RP + row] = l_run[rt];
-      }
-    }
-  };
-  auto take = [&](int slot) {
-    const float* o = s_slab + slot * RP * D;
-    const float* ml = s_ml + slot * 2 * RP;
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int row = l16 + 16 * rt;
-      const float mo = ml[row], lo = ml[RP + row];
-      const float M = fmaxf(m_run[rt], mo);
-      const float fa = M == -INFINITY ? 0.f : fast_exp2(m_run[rt] - M);
-      const float fb = M == -INFINITY ? 0.f : fast_exp2(mo - M);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[rt][mt] = acc[rt][mt] * fa +
-                      *(const f4v*)(o + row * D + 16 * mt + 4 * gq) * fb;
-      l_run[rt] = l_run[rt] * fa + lo * fb;
-      m_run[rt] = M;
-    }
-  };
-  __syncthreads();   // the loop's LDS (q, B operands) is reused below
-  if (wave >= 2) put(wave - 2);
-  __syncthreads();
-  if (wave < 2) take(wave);
-  __syncthreads();
-  if (wave == 1) put(0);
-  __syncthreads();
-  if (wave == 0) take(0);
-
   // ---- workgroup partial: o[RP][D], m[RP], l[RP]
-  const int64_t pstride = (int64_t)RP * (D + 2);
-  float* pblk = a.ws + blk * a.s_alloc * pstride;
-  if (wave == 0) {
-    float* po = pblk + split * pstride;
+  if (strm == 0) {
+    const int64_t pstride = (int64_t)RP * (D + 2);
+    float* po = a.ws + (blk * a.s_alloc + split) * pstride;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int row = l16 + 16 * rt;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        *(f4v*)(po + row * D + 16 * mt + 4 * gq) = acc[rt][mt];
-      if (gq == 0) {
-        po[RP * D + row] = m_run[rt];
-        po[RP * D + RP + row] = l_run[rt];
-      }
+    for (int mt = 0; mt < MT; ++mt)
+      *(f4v*)(po + row * D + 16 * mt + 4 * gq) = acc[mt];
+    if (gq == 0) {
+      po[RP * D + row] = m_ref;
+      po[RP * D + RP + row] = l_run;
     }
   }
 }
 
-template <int PATH, int D, int NRT, int NG>
-hipError_t go(const AttnArgs& a, hipStream_t s) {
-  const int64_t nb = (int64_t)a.g.B * a.g.Hkv;
-  using C = Cfg<PATH, D, NRT, NG>;
-  const size_t lds = Lds<C::RP, D, NRT, C::KS>::bytes(a.ngr);
-  if (lds > 64 * 1024) {
-    static bool raised = false;   // once per instantiation
-    if (!raised) {
-      hipError_t e = hipFuncSetAttribute(
-          (const void*)attn_kernel<PATH, D, NRT, NG>,
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
+constexpr int kMaxDevices = 64;
+
+// Workgroups of one instantiation resident per CU on `dev` (0 if unknown).
+template <int PATH, int D, int NG, bool PAIR>
+int occupancy(int dev) {
+  using C = Cfg<PATH, D, NG, PAIR>;
+  static int cache[kMaxDevices];   // 0 = not queried yet
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  if (cache[dev] == 0) {
+    hipError_t e = hipFuncSetAttribute(
+        (const void*)attn_kernel<PATH, D, NG, PAIR>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return 0;
+    int n = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &n, (const void*)attn_kernel<PATH, D, NG, PAIR>, C::NW * kWave, C::LDS);
+    if (e != hipSuccess || n < 1) return 0;
+    cache[dev] = n;
   }
-  hipLaunchKernelGGL((attn_kernel<PATH, D, NRT, NG>),
-                     dim3((unsigned)(nb * (a.s_q + a.s_r))), dim3(NT), lds, s, a);
-  hipError_t e = hipGetLastError();
+  return cache[dev];
+}
+
+template <int PATH, int D, int NG, bool PAIR>
+hipError_t go(AttnArgs a, hipStream_t s) {
+  using C = Cfg<PATH, D, NG, PAIR>;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<D, 16 * NRT>), dim3((unsigned)(nb * a.rows)),
-                     dim3(NT), 0, s, a);
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int occ = occupancy<PATH, D, NG, PAIR>(dev);
+  if (occ < 1) return hipErrorInvalidConfiguration;
+  const int64_t nb = (int64_t)a.g.B * a.g.Hkv;
+  const int64_t units = 2 * cdiv(a.n_r, kTile) + cdiv(a.n_q / kTile, C::TPU);
+  a.S = plan_splits(nb, (int64_t)cus * occ, units, C::NS, a.s_alloc);
+  hipLaunchKernelGGL((attn_kernel<PATH, D, NG, PAIR>),
+                     dim3((unsigned)(nb * a.S)), dim3(C::NW * kWave), C::LDS, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<D, C::RP>), dim3((unsigned)(nb * a.rows)),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int PATH, int D, int NRT>
+template <int PATH, int D, bool PAIR>
 hipError_t by_ng(const AttnArgs& a, hipStream_t s) {
   switch (a.g.d / a.g.Gv) {
-    case 1: return go<PATH, D, NRT, 1>(a, s);
-    case 2: return go<PATH, D, NRT, 2>(a, s);
-    case 4: return go<PATH, D, NRT, 4>(a, s);
+    case 1: return go<PATH, D, 1, PAIR>(a, s);
+    case 2: return go<PATH, D, 2, PAIR>(a, s);
+    case 4: return go<PATH, D, 4, PAIR>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int PATH, int D>
 hipError_t by_rows(const AttnArgs& a, hipStream_t s) {
-  return a.rows_pad == 16 ? by_ng<PATH, D, 1>(a, s) : by_ng<PATH, D, 2>(a, s);
+  return a.rows_pad == 16 ? by_ng<PATH, D, false>(a, s) : by_ng<PATH, D, true>(a, s);
 }
 
 }  // namespace
+
+// Splits per block: enough workgroups to fill every resident slot once,
+// choosing among 1x..4x the minimum the count whose last dispatch wave is
+// fullest; no more than one split per `streams` units and no more than cap.
+int plan_splits(int64_t nb, int64_t slots, int64_t units, int streams, int cap) {
+  const int64_t smin = cdiv(slots, nb);
+  int64_t best = smin;
+  double best_eff = -1.0;
+  for (int64_t s = smin; s <= 4 * smin; ++s) {
+    const int64_t wg = nb * s;
+    const double eff = (double)wg / (double)(slots * cdiv(wg, slots));
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = s;
+    }
+  }
+  const int64_t by_units = cdiv(units, streams);
+  if (best > by_units) best = by_units;
+  if (best > cap) best = cap;
+  return best < 1 ? 1 : (int)best;
+}
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int bits = a.g.bits, d = a.g.d;

@@ -102,21 +102,18 @@ struct AttnArgs {
   const __half* q;
   __half* out;
   float* lse;
-  float* ws;        // partials workspace (after the ticket area)
-  unsigned* tickets;
+  float* ws;        // partials: [B*Hkv][s_alloc][rows_pad][d + 2] float
   int64_t n_q, n_r;
   int T, Hq, gs, rows;
   int path;         // KVQ_TARGET / KVQ_DRAFT4
   float c0;         // sm_scale * log2(e)
-  // split plan
-  int waves;        // waves per workgroup
-  int tpw;          // quantized tiles per wave
-  int s_q;          // quantized-split workgroups per block
-  int s_r;          // residual workgroups per block
+  int S;            // split workgroups per block (set by the launcher)
   int s_alloc;      // partial slots per block in the workspace
-  int ngr;          // key groups per round of 4 tiles: max(1, 128/G)
   int rows_pad;     // 16 * row tiles
 };
+// Splits per block for nb blocks on `slots` resident workgroup slots, with
+// `units` units of work per block, nw waves per workgroup, at most cap.
+int plan_splits(int64_t nb, int64_t slots, int64_t units, int nw, int cap);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
 struct TopkArgs {
