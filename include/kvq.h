@@ -137,8 +137,9 @@ typedef struct kvq_cache {
  * set n_q = n_r = 0.  Host only.  Shape rules: B, Hkv >= 1; d in {64, 128};
  * bits in {8, 2, 1} (bits == 1 needs d == 128); G a positive multiple of
  * 32; L_max a positive multiple of G, at most 2^24; Gv a multiple of 16
- * dividing d with d/Gv <= 4; G <= R; 1 <= max_append.  The ring needs no initial contents.
- * KVQ_EINVAL (message in kv_last_error) when a rule fails. */
+ * dividing d with d/Gv <= 4; G <= R; 1 <= max_append.  The ring needs no
+ * initial contents.  KVQ_EINVAL (message in kv_last_error) when a rule
+ * fails. */
 int kv_cache_layout(kvq_cache* c);
 
 /* Quantize-on-append ([QS] Approach; quantizer and grouping as above).
@@ -157,7 +158,11 @@ int kv_quant_append(kvq_cache* c, const void* k_new, const void* v_new, int n,
  * Host only. */
 int kv_rollback(kvq_cache* c, int m);
 
-/* Workspace bytes kv_attn_verify needs for this cache at any fill level. */
+/* Workspace bytes kv_attn_verify needs for this cache at any fill level:
+ * one fp32 partial (m, l, o for up to 32 rows) per split of every block,
+ * for as many splits as the launcher may choose on a device with up to 512
+ * resident workgroup slots (it uses fewer on larger devices).  0 if the
+ * shape is invalid.  Host only. */
 size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq);
 
 /* Speculative verify / draft attention ([QS] Approach; [SC] Approach for
@@ -172,9 +177,12 @@ size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq);
  *   residual tokens); out = softmax(logits) . v^, fp32 accumulation.
  *   out: device fp16 [B][T][Hq][d].  lse: device fp32 [B][Hq][T] natural-log
  *   log-sum-exp of the logits, or NULL.
- *   ws: device workspace of >= kv_attn_workspace_bytes(c, T, Hq) bytes,
- *   zero-filled before its first use; every call leaves it reusable.
- *   Calls sharing one ws must be ordered (same stream).
+ *   ws: device workspace of >= kv_attn_workspace_bytes(c, T, Hq) bytes;
+ *   it needs no initial contents and holds scratch between the call's two
+ *   launches (split pass, then log-sum-exp merge).  Calls sharing one ws
+ *   must be ordered (same stream).
+ *   Range: value groups need scale s <= 63 (the PV step multiplies fp16
+ *   probabilities scaled to at most 2^10 by s in fp16); every input finite.
  * Requires 1 <= T <= 16, T <= n_r, Hq % Hkv == 0, (Hq/Hkv)*T <= 32. */
 int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq, int path,
                    float sm_scale, void* out, float* lse, void* ws,

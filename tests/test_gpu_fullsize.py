@@ -1,0 +1,177 @@
+"""GPU parity at the full sizes of the benchmark workloads, through the same
+C-ABI calls and launch configuration bench.py times.
+
+The whole cache is built on the GPU: the sampled (b, kvh) blocks take their
+tokens from the seeded generator (kvq_synth), every other block from a
+seeded on-device normal draw (any finite tokens: blocks never interact).
+The outputs of the sampled blocks (attention rows, LSE, top-k indices and
+keys) are compared with the oracle run on those blocks alone, following the
+same sequence of appends and rollbacks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth as synth
+import quantized_kv_attention_quant_amd as kq
+from oracle import attention, cache as ocache, topk as otopk
+from kvq_testlib import assert_attn_close, lse_tolerance, say, shape_for
+
+pytestmark = pytest.mark.gpu
+
+
+def device_tokens(w, seed, L, sampled):
+    """fp16 device K, V [B][L][Hkv][d] and the host tokens of `sampled`."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1_000_003 * seed + 17)
+    K = torch.empty((w.B, L, w.Hkv, w.d), dtype=torch.float16, device="cuda")
+    V = torch.empty_like(K)
+    for b in range(w.B):              # one batch row at a time (memory)
+        K[b] = torch.randn((L, w.Hkv, w.d), generator=g, device="cuda").half()
+        V[b] = torch.randn((L, w.Hkv, w.d), generator=g, device="cuda").half()
+    host = {}
+    for (b, h) in sampled:
+        kb, vb = synth.kv_block(w, seed, b, h, L)
+        K[b, :, h] = torch.from_numpy(kb).cuda()
+        V[b, :, h] = torch.from_numpy(vb).cuda()
+        host[(b, h)] = (kb, vb)
+    torch.cuda.synchronize()
+    return K, V, host
+
+
+class Mirror:
+    """Oracle replays of the sampled blocks, fed the same appends."""
+
+    def __init__(self, w, host):
+        self.w, self.host = w, host
+        self.rep = {bh: ocache.Replay(1, 1, w.d, w.G, w.Gv, w.bits, w.R)
+                    for bh in host}
+
+    def append(self, p0, p1):
+        for bh, (kb, vb) in self.host.items():
+            self.rep[bh].append(kb[None, p0:p1, None], vb[None, p0:p1, None])
+
+    def rollback(self, m):
+        for r in self.rep.values():
+            r.rollback(m)
+
+
+def check_attention(cache, mirror, q16, path, label):
+    """Run kv_attn_verify on the whole cache; compare the sampled blocks."""
+    w = mirror.w
+    gs = w.Hq // w.Hkv
+    out, lse = cache.verify(torch.from_numpy(q16).cuda(), path=path,
+                            want_lse=True)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for (b, h), rep in mirror.rep.items():
+        assert (rep.n_q, rep.n_r) == (cache.n_q, cache.n_r)
+        qb = q16[b:b + 1, :, h * gs:(h + 1) * gs]
+        ref, ref_lse = attention.attend(rep, qb, path, w.d ** -0.5)
+        got = out[b:b + 1, :, h * gs:(h + 1) * gs]
+        rel = assert_attn_close(got, ref, f"{label} block ({b},{h})")
+        tol = lse_tolerance(rep, qb, path, w.d ** -0.5)
+        lerr = np.abs(lse[b:b + 1, h * gs:(h + 1) * gs] - ref_lse)
+        say(f"    {label} ({b},{h}): rel err {rel:.2e}, lse err "
+            f"{lerr.max():.2e}")
+        assert (lerr <= tol).all(), (label, b, h)
+    return out
+
+
+def test_llama2_8k_verify_t9_and_draft():
+    w = synth.WORKLOADS["llama2_7b_8k"]
+    say("[gpu] full size llama2_7b_8k: INT8 T=9, INT4 draft T=1")
+    sampled = [(0, 0), (0, 13), (0, 31)]
+    K, V, host = device_tokens(w, 0, w.L, sampled)
+    cache = kq.QuantKVCache(shape_for(w, max_append=32))
+    mirror = Mirror(w, host)
+    cache.append(K[:, :w.L - 9].contiguous(), V[:, :w.L - 9].contiguous())
+    mirror.append(0, w.L - 9)
+    cache.append(K[:, w.L - 9:].contiguous(), V[:, w.L - 9:].contiguous())
+    mirror.append(w.L - 9, w.L)
+    check_attention(cache, mirror, synth.queries(w, 1, 9), "target", "T=9")
+    check_attention(cache, mirror, synth.queries(w, 2, 1), "draft4", "draft")
+
+
+def test_llama3_32k_bench_step():
+    """The benchmark step: append 7, INT4 draft T=1, INT8 verify T=7,
+    rollback 7; the step repeated gives bit-identical outputs."""
+    w = synth.WORKLOADS["llama3_8b_32k"]
+    say("[gpu] full size llama3_8b_32k: bench step x2")
+    sampled = [(0, 0), (0, 5)]
+    K, V, host = device_tokens(w, 0, w.L, sampled)
+    cache = kq.QuantKVCache(shape_for(w, max_append=32))
+    mirror = Mirror(w, host)
+    L0 = w.L - 7
+    cache.append(K[:, :L0].contiguous(), V[:, :L0].contiguous())
+    mirror.append(0, L0)
+    base = (cache.n_q, cache.n_r)
+    qd, qv = synth.queries(w, 0, 1), synth.queries(w, 1, 7)
+    cache.append(K[:, L0:].contiguous(), V[:, L0:].contiguous())
+    mirror.append(L0, w.L)
+    d0 = check_attention(cache, mirror, qd, "draft4", "draft")
+    t0 = check_attention(cache, mirror, qv, "target", "verify")
+    cache.rollback(7)
+    assert (cache.n_q, cache.n_r) == base
+    cache.append(K[:, L0:].contiguous(), V[:, L0:].contiguous())
+    d1, _ = cache.verify(torch.from_numpy(qd).cuda(), path="draft4")
+    t1, _ = cache.verify(torch.from_numpy(qv).cuda(), path="target")
+    torch.cuda.synchronize()
+    assert np.array_equal(d0, d1.cpu().numpy())
+    assert np.array_equal(t0, t1.cpu().numpy())
+
+
+def test_lwm_128k_append6_rollback2():
+    """Quantize-on-append of 6 tokens per step, verify T=6 and T=1..5 rows,
+    INT4 draft, rollback 2 (flushes happen inside the steps)."""
+    w = synth.WORKLOADS["lwm_7b_128k"]
+    say("[gpu] full size lwm_7b_128k: append 6 / verify / rollback 2")
+    sampled = [(0, 7)]
+    K, V, host = device_tokens(w, 0, w.L, sampled)
+    cache = kq.QuantKVCache(shape_for(w, max_append=32))
+    mirror = Mirror(w, host)
+    p = w.L - 3 * 6 + 2 * 2           # three steps end exactly at L
+    cache.append(K[:, :p].contiguous(), V[:, :p].contiguous())
+    mirror.append(0, p)
+    for step, T in enumerate((6, 3, 1)):
+        cache.append(K[:, p:p + 6].contiguous(), V[:, p:p + 6].contiguous())
+        mirror.append(p, p + 6)
+        p += 6
+        check_attention(cache, mirror, synth.queries(w, 10 + step, T),
+                        "target", f"step {step} T={T}")
+        if step == 0:
+            check_attention(cache, mirror, synth.queries(w, 20, 1), "draft4",
+                            "step 0 draft")
+        if step < 2:
+            cache.rollback(2)
+            mirror.rollback(2)
+            p -= 2
+    assert p == w.L
+
+
+@pytest.mark.parametrize("name", ["specache_1bit", "specache_2bit"])
+def test_specache_batched_attention_and_topk(name):
+    w = synth.WORKLOADS[name]
+    say(f"[gpu] full size {name}: B=36 T=2 attention + top-64")
+    sampled = [(0, 0), (17, 3), (35, 7)]
+    K, V, host = device_tokens(w, 0, w.L, sampled)
+    cache = kq.QuantKVCache(shape_for(w, max_append=32))
+    mirror = Mirror(w, host)
+    cache.append(K[:, :w.L - 2].contiguous(), V[:, :w.L - 2].contiguous())
+    mirror.append(0, w.L - 2)
+    cache.append(K[:, w.L - 2:].contiguous(), V[:, w.L - 2:].contiguous())
+    mirror.append(w.L - 2, w.L)
+    q16 = synth.queries(w, 3, 2)
+    check_attention(cache, mirror, q16, "target", "T=2")
+    qs16 = np.ascontiguousarray(q16[:, 1])          # the speculative token
+    idx, key = cache.topk(torch.from_numpy(qs16).cuda(), w.topk)
+    torch.cuda.synchronize()
+    idx, key = idx.cpu().numpy(), key.cpu().numpy()
+    gs = w.Hq // w.Hkv
+    for (b, h), rep in mirror.rep.items():
+        ref_i, ref_k = otopk.topk_block(qs16[b, h * gs:(h + 1) * gs],
+                                        rep.kq[0, 0], rep.ks[0, 0],
+                                        rep.kz[0, 0], w.G, "target", w.topk)
+        assert np.array_equal(idx[b, h], ref_i), (b, h)
+        assert np.array_equal(key[b, h].view(np.uint32),
+                              ref_k.view(np.uint32)), (b, h)
