@@ -281,15 +281,16 @@ __device__ __forceinline__ void wait_le(int pending) {
   }
 }
 
-// Per-path geometry.  Every wave owns one 16-row tile of the block's rows.
-// Up to 16 rows (SOLO) every wave streams its own run of units; with 17..32
-// rows (PAIR) two waves share one stream, wave h of the pair taking rows
-// 16h .. 16h+15, so the per-wave state (B operands, accumulators) is that
-// of 16 rows and two waves fit on every SIMD.
-template <int PATH, int D, int NG, bool PAIR>
+// Per-path geometry.  A wave owns NRT 16-row tiles of the block's rows.
+// SOLO streams (every wave its own run of units) carry NRT = 1 or 2 row
+// tiles per wave; PAIR streams (17..32 rows) let two waves share one run,
+// wave h taking row tile h, so each wave's state is that of 16 rows.
+template <int PATH, int D, int NG, int NRT, bool PAIR>
 struct Cfg {
-  static constexpr int NH = PAIR ? 2 : 1;        // row tiles per stream
-  static constexpr int RP = 16 * NH;             // staged (padded) rows
+  static_assert(NRT == 1 || (NRT == 2 && !PAIR), "row tiles per wave");
+  static constexpr int NH = PAIR ? 2 : 1;        // waves per stream
+  static constexpr int RTT = NH * NRT;           // row tiles per stream
+  static constexpr int RP = 16 * RTT;            // staged (padded) rows
   static constexpr int W = PATH == P_L2 ? 2 : PATH == P_L1 ? 1 : 4;
   static constexpr bool TWO = PATH == P_T8;      // hi + lo planes
   static constexpr bool LOW = PATH == P_L2 || PATH == P_L1;
@@ -318,26 +319,31 @@ struct Cfg {
   static constexpr int NIR = dma_count(RESU);
   static constexpr int QB = RP * D * 2;          // staged q rows (fp16)
   // waves per workgroup: 8 (two per SIMD) unless eight solo streams of two
-  // stages do not fit the LDS
-  static constexpr int NW = PAIR || 16 * STAGE + QB <= kLdsBytes ? 8 : 4;
-  static constexpr int NS = PAIR ? NW / 2 : NW;  // unit streams per workgroup
+  // stages do not fit the LDS, or a wave holds two row tiles (its state
+  // then needs more than the 256 registers of two waves per SIMD)
+  static constexpr int NW =
+      NRT == 1 && (PAIR || 16 * STAGE + QB <= kLdsBytes) ? 8 : 4;
+  static constexpr int NS = NW / NH;             // unit streams per workgroup
   static constexpr int ST0 = (kLdsBytes - QB) / (NS * STAGE);
   static constexpr int ST = ST0 > 4 ? 4 : ST0;
   static constexpr int LDS = NS * ST * STAGE + QB;
-  static constexpr int MERGE = (NS / 2) * NH * 16 * (D + 4 + 2) * 4;
+  static constexpr int DP = D + 4;               // merge slab row (floats)
+  static constexpr int MERGE = (NS / 2) * RTT * 16 * (DP + 2) * 4;
   static_assert(ST >= (PAIR ? 3 : 2), "stages per stream");
   static_assert((ST - 1) * (NIQ > NIR ? NIQ : NIR) <= 63, "vmcnt range");
   static_assert(MERGE <= NS * ST * STAGE, "merge slabs fit the stage area");
 };
 
 // Merge kernel, one workgroup per (block, row): combines the row's S split
-// partials by log-sum-exp with every thread busy: per-split (m, l) into LDS,
-// wave reductions for the row max and sum, then the o rows summed by NT/D
-// thread groups, each with 8 loads in flight.
+// partials by log-sum-exp.  Every thread first issues the loads of its
+// share of the o rows (up to PRE per thread) and of the (m, l) pairs, so
+// the whole kernel waits on one round trip; the row max and sum are wave
+// reductions through LDS, the o rows are summed by NT/D thread groups.
 template <int D, int RP>
 __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
   constexpr int NT = 256;
   constexpr int NPART = NT / D;          // thread groups over the splits
+  constexpr int PRE = 16;                // o values loaded up front
   __shared__ float lds[2 * 1024 + 8 + NT];
   const int S = a.S;
   const int64_t blk = blockIdx.x / a.rows;
@@ -349,41 +355,44 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
   float* sl = lds + S;          // [S] l
   float* red = lds + 2 * S;     // [8] wave partials
   float* part = red + 8;        // [NPART][D]
-  for (int s = tid; s < S; s += NT) {
-    sm[s] = pblk[s * pstride + RP * D + row];
-    sl[s] = pblk[s * pstride + RP * D + RP + row];
+  const int c = tid % D, pg = tid / D;
+  const float* src = pblk + row * D + c;
+  float x[PRE];
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const int sp = pg + k * NPART;
+    x[k] = sp < S ? src[sp * pstride] : 0.f;
+  }
+  for (int sp = tid; sp < S; sp += NT) {
+    sm[sp] = pblk[sp * pstride + RP * D + row];
+    sl[sp] = pblk[sp * pstride + RP * D + RP + row];
   }
   __syncthreads();
   float M = -INFINITY;
-  for (int s = tid; s < S; s += NT) M = fmaxf(M, sm[s]);
+  for (int sp = tid; sp < S; sp += NT) M = fmaxf(M, sm[sp]);
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
   if ((tid & (kWave - 1)) == 0) red[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float ls = 0.f;
-  for (int s = tid; s < S; s += NT) {
-    const float e = sm[s] == -INFINITY ? 0.f : fast_exp2(sm[s] - M);
-    sm[s] = e;
-    ls += sl[s] * e;
+  for (int sp = tid; sp < S; sp += NT) {
+    const float e = sm[sp] == -INFINITY ? 0.f : fast_exp2(sm[sp] - M);
+    sm[sp] = e;
+    ls += sl[sp] * e;
   }
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) ls += __shfl_xor(ls, o);
   if ((tid & (kWave - 1)) == 0) red[4 + wave] = ls;
   __syncthreads();
   const float lsum = (red[4] + red[5]) + (red[6] + red[7]);
-  const int c = tid % D, pg = tid / D;
-  const float* src = pblk + row * D + c;
   float o = 0.f;
-  int s = pg;
-  for (; s + 7 * NPART < S; s += 8 * NPART) {
-    float x[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = src[(s + k * NPART) * pstride];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) o += sm[s + k * NPART] * x[k];
+  for (int k = 0; k < PRE; ++k) {
+    const int sp = pg + k * NPART;
+    if (sp < S) o += sm[sp] * x[k];
   }
-  for (; s < S; s += NPART) o += sm[s] * src[s * pstride];
+  for (int sp = pg + PRE * NPART; sp < S; sp += NPART) o += sm[sp] * src[sp * pstride];
   part[pg * D + c] = o;
   __syncthreads();
   const int b = (int)(blk / a.g.Hkv), kvh = (int)(blk % a.g.Hkv);
@@ -402,11 +411,12 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
 //   stages  [NS][ST][STAGE]   each stream's ring of units
 //   s_q     fp16 [RP][D]      this block's query rows (zero past `rows`)
 // After the unit loop the stage area holds the stream-merge slabs
-//   slab float [NS/2][NH][16][D+4], ml float [NS/2][NH][2][16].
-template <int PATH, int D, int NG, bool PAIR>
-__global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
-  using C = Cfg<PATH, D, NG, PAIR>;
-  constexpr int KS = C::KS, MT = C::MT, ST = C::ST, NS = C::NS, NH = C::NH;
+//   slab float [NS/2][RTT][16][D+4], ml float [NS/2][RTT][2][16].
+template <int PATH, int D, int NG, int NRT, bool PAIR>
+__global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
+    attn_kernel(const AttnArgs a) {
+  using C = Cfg<PATH, D, NG, NRT, PAIR>;
+  constexpr int KS = C::KS, MT = C::MT, ST = C::ST, NS = C::NS, RTT = C::RTT;
   constexpr int RP = C::RP;
   constexpr int NT = C::NW * kWave;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -422,7 +432,10 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
   const int h = PAIR ? wave & 1 : 0;             // row tile of this wave
   const bool loader = h == 0;                    // issues the stream's copies
   const int lane = tid % kWave, l16 = lane & 15, gq = lane >> 4;
-  const int row = l16 + 16 * h;                  // this lane's row
+  // this lane's row in row tile rt of the wave
+  auto row_of = [&](int rt) __attribute__((always_inline)) {
+    return l16 + 16 * (h * NRT + rt);
+  };
   const unsigned lane16 = 16u * lane;
   const int L = (int)(a.n_q + a.n_r);
 
@@ -437,7 +450,9 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
     return v;
   };
   const int64_t c0s = (int64_t)split * NS;
-  const int u0 = bound(c0s + strm), u1 = bound(c0s + strm + 1);
+  // wave-uniform: keep them (and everything derived) in scalar registers
+  const int u0 = __builtin_amdgcn_readfirstlane(bound(c0s + strm));
+  const int u1 = __builtin_amdgcn_readfirstlane(bound(c0s + strm + 1));
 
   unsigned char* stages = smem + strm * ST * C::STAGE;
   const unsigned lds_stages = (unsigned)(uintptr_t)stages;
@@ -528,128 +543,165 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
     }
   }
 
-  // ---- per-wave state (one 16-row tile)
-  float m_ref = -INFINITY, sig = 0.f, l_run = 0.f, binit = 0.f;
-  f4v cinit = f4v{0.f, 0.f, 0.f, 0.f};
-  f4v acc[MT];
-  float zacc[NG];
-  u4v bqh[KS], bql[KS];                // B operands Q' = hi + lo
-  u4v bpres = u4v{0u, 0u, 0u, 0u};     // ring tile: P' between its two units
+  // ---- per-wave state (NRT 16-row tiles)
+  float m_ref[NRT], sig[NRT], l_run[NRT], binit[NRT];
+  f4v cinit[NRT];
+  f4v acc[NRT][MT];
+  float zacc[NRT][NG];
+  u4v bqh[NRT][KS], bql[NRT][KS];      // B operands Q' = hi + lo
+  u4v bpres[NRT];                      // ring tile: P' between its two units
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4v{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < NRT; ++rt) {
+    m_ref[rt] = -INFINITY;
+    sig[rt] = l_run[rt] = binit[rt] = 0.f;
+    cinit[rt] = f4v{0.f, 0.f, 0.f, 0.f};
+    bpres[rt] = u4v{0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int gg = 0; gg < NG; ++gg) zacc[gg] = 0.f;
+    for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) bqh[ks] = bql[ks] = u4v{0u, 0u, 0u, 0u};
+    for (int gg = 0; gg < NG; ++gg) zacc[rt][gg] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bqh[rt][ks] = bql[rt][ks] = u4v{0u, 0u, 0u, 0u};
+  }
   int cur_grp = -2;                    // -1: ring operands, >= 0: key group
   const DecK dk = dec_consts();
   const float c0 = a.c0;
-  const __half* qrow = s_q + row * D;
-  // q * c0 of the channels this lane multiplies in key-group operands:
-  // (cA(ks) + j, cB(ks) + j), fixed for the whole run
+  // channels this lane multiplies in key-group operands: (cA(ks) + j,
+  // cA(ks) + DAB + j), j = 0..3
   auto chan_a = [&](int ks) __attribute__((always_inline)) {
     if constexpr (C::W == 4) return gq * (D / 4) + 8 * ks;
     else if constexpr (C::W == 2) return gq * (D / 4) + 16 * (ks / 2) + 4 * (ks % 2);
     else return gq * (D / 4) + 4 * ks;
   };
   constexpr int DAB = C::W == 4 ? 4 : C::W == 2 ? 8 : 16;   // cB - cA
-  float qcA[KS][4], qcB[KS][4];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const u2v qa = *(const u2v*)(qrow + chan_a(ks));
-    const u2v qb = *(const u2v*)(qrow + chan_a(ks) + DAB);
+  // With one row tile, q * c0 of those channels stays in registers for the
+  // whole run; with two it is re-read from LDS per key group (registers).
+  constexpr bool QC = NRT == 1;
+  float qcA[QC ? KS : 1][4], qcB[QC ? KS : 1][4];
+  auto load_qc = [&](int rt, int ks, float* fa, float* fb)
+      __attribute__((always_inline)) {
+    const __half* qr = s_q + row_of(rt) * D;
+    const u2v qa = *(const u2v*)(qr + chan_a(ks));
+    const u2v qb = *(const u2v*)(qr + chan_a(ks) + DAB);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      qcA[ks][j] = h_at(qa, j) * c0;
-      qcB[ks][j] = h_at(qb, j) * c0;
+      fa[j] = h_at(qa, j) * c0;
+      fb[j] = h_at(qb, j) * c0;
     }
+  };
+  if constexpr (QC) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) load_qc(0, ks, qcA[ks], qcB[ks]);
   }
 
-  auto refresh = [&]() __attribute__((always_inline)) {
-    const float v = binit + sig;
-    cinit = f4v{v, v, v, v};
+  auto refresh = [&](int rt) __attribute__((always_inline)) {
+    const float v = binit[rt] + sig[rt];
+    cinit[rt] = f4v{v, v, v, v};
   };
 
   // B operands of the fp16 ring: q * c0 over natural channel pairs
   // (2j, 2j+1) of each 8-channel k-step slice.
   auto build_res = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u4v q8 = *(const u4v*)(qrow + gq * (D / 4) + 8 * ks);
-      unsigned hi[4], lo[4];
+    for (int rt = 0; rt < NRT; ++rt) {
+      const __half* qr = s_q + row_of(rt) * D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float xa = opaque(h_lo(q8[j]) * c0);
-        const float xb = opaque(h_hi(q8[j]) * c0);
-        hi[j] = pack2(xa, xb);
-        lo[j] = pack2(xa - h_lo(hi[j]), xb - h_hi(hi[j]));
+      for (int ks = 0; ks < KS; ++ks) {
+        const u4v q8 = *(const u4v*)(qr + gq * (D / 4) + 8 * ks);
+        unsigned hi[4], lo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float xa = opaque(h_lo(q8[j]) * c0);
+          const float xb = opaque(h_hi(q8[j]) * c0);
+          hi[j] = pack2(xa, xb);
+          lo[j] = pack2(xa - h_lo(hi[j]), xb - h_hi(hi[j]));
+        }
+        bqh[rt][ks] = u4v{hi[0], hi[1], hi[2], hi[3]};
+        bql[rt][ks] = u4v{lo[0], lo[1], lo[2], lo[3]};
       }
-      bqh[ks] = u4v{hi[0], hi[1], hi[2], hi[3]};
-      bql[ks] = u4v{lo[0], lo[1], lo[2], lo[3]};
+      binit[rt] = 0.f;
+      refresh(rt);
     }
-    binit = 0.f;
-    refresh();
   };
 
   // B operands of one key group: Q' = q * c0 * s over the channel pairs the
-  // code decoder produces for k-step ks: (cA + j, cB + j), j = 0..3; the
-  // accumulator start is  sum_c q c0 z - KBIAS * sum_c Q'  (the second sum
-  // by MFMA against a constant operand, over the same fp16 parts).
+  // code decoder produces for k-step ks; the accumulator start is
+  // sum_c q c0 z - KBIAS * sum_c Q'  (the second sum by MFMA against a
+  // constant operand, over the same fp16 parts).
   auto build_quant = [&](const unsigned char* ksz) __attribute__((always_inline)) {
-    float zs = 0.f;
+    float zs[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) zs[rt] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int cA = chan_a(ks);
       const u4v sA = *(const u4v*)(ksz + 4 * cA);          // {s, z} of cA .. cA+3
       const u4v sB = *(const u4v*)(ksz + 4 * (cA + DAB));
-      unsigned hi[4], lo[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // fma with +0 keeps the fp16 operand unconverted (mixed fma)
-        const float xa = opaque(__builtin_fmaf(qcA[ks][j], h_lo(sA[j]), 0.f));
-        const float xb = opaque(__builtin_fmaf(qcB[ks][j], h_lo(sB[j]), 0.f));
-        hi[j] = pack2(xa, xb);
-        lo[j] = pack2(__builtin_fmaf(h_lo(hi[j]), -1.f, xa),
-                      __builtin_fmaf(h_hi(hi[j]), -1.f, xb));
-        zs = __builtin_fmaf(qcA[ks][j], h_hi(sA[j]), zs);
-        zs = __builtin_fmaf(qcB[ks][j], h_hi(sB[j]), zs);
-      }
-      bqh[ks] = u4v{hi[0], hi[1], hi[2], hi[3]};
-      bql[ks] = u4v{lo[0], lo[1], lo[2], lo[3]};
-    }
-    const float z = sum_x4(zs);
-    f4v cc = f4v{z, z, z, z};
-    if constexpr (C::KBIAS != 0.f) {
-      const u4v kn = u4v{C::NEG, C::NEG, C::NEG, C::NEG};
+      for (int rt = 0; rt < NRT; ++rt) {
+        float fa[4], fb[4];
+        if constexpr (QC) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        cc = mfma16(kn, bqh[ks], cc);
-        cc = mfma16(kn, bql[ks], cc);
+          for (int j = 0; j < 4; ++j) { fa[j] = qcA[ks][j]; fb[j] = qcB[ks][j]; }
+        } else {
+          load_qc(rt, ks, fa, fb);
+        }
+        unsigned hi[4], lo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // fma with +0 keeps the fp16 operand unconverted (mixed fma)
+          const float xa = opaque(__builtin_fmaf(fa[j], h_lo(sA[j]), 0.f));
+          const float xb = opaque(__builtin_fmaf(fb[j], h_lo(sB[j]), 0.f));
+          hi[j] = pack2(xa, xb);
+          lo[j] = pack2(__builtin_fmaf(h_lo(hi[j]), -1.f, xa),
+                        __builtin_fmaf(h_hi(hi[j]), -1.f, xb));
+          zs[rt] = __builtin_fmaf(fa[j], h_hi(sA[j]), zs[rt]);
+          zs[rt] = __builtin_fmaf(fb[j], h_hi(sB[j]), zs[rt]);
+        }
+        bqh[rt][ks] = u4v{hi[0], hi[1], hi[2], hi[3]};
+        bql[rt][ks] = u4v{lo[0], lo[1], lo[2], lo[3]};
       }
     }
-    binit = cc[0];
-    refresh();
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const float z = sum_x4(zs[rt]);
+      f4v cc = f4v{z, z, z, z};
+      if constexpr (C::KBIAS != 0.f) {
+        const u4v kn = u4v{C::NEG, C::NEG, C::NEG, C::NEG};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          cc = mfma16(kn, bqh[rt][ks], cc);
+          cc = mfma16(kn, bql[rt][ks], cc);
+        }
+      }
+      binit[rt] = cc[0];
+      refresh(rt);
+    }
   };
 
   // S^T = K Q'^T for the two 16-token subtiles, started at cinit.
-  auto scores = [&](f4v (&sc)[2], const u4v (&ak)[2][KS]) {
-    sc[0] = sc[1] = cinit;
+  auto scores = [&](f4v (&sc)[2][NRT], const u4v (&ak)[2][KS])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) sc[0][rt] = sc[1][rt] = cinit[rt];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        sc[st] = mfma16(ak[st][ks], bqh[ks], sc[st]);
-        sc[st] = mfma16(ak[st][ks], bql[ks], sc[st]);
-      }
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          sc[st][rt] = mfma16(ak[st][ks], bqh[rt][ks], sc[st][rt]);
+          sc[st][rt] = mfma16(ak[st][ks], bql[rt][ks], sc[st][rt]);
+        }
   };
 
-  // Online softmax over the 8 scores this lane holds (taken relative to the
-  // row reference, + kPExp); returns p' in place.  Fast path: every score
-  // of the wave is within kTau of its row reference.
-  auto softmax = [&](f4v& s0, f4v& s1) __attribute__((always_inline)) {
+  // Online softmax over the 8 scores this lane holds for row tile rt
+  // (taken relative to the row reference, + kPExp); returns p' in place.
+  // Fast path: every score of the wave is within kTau of its reference.
+  auto softmax = [&](int rt, f4v& s0, f4v& s1) __attribute__((always_inline)) {
     const float lm = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                            fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-    const bool fin = m_ref != -INFINITY;
+    const bool fin = m_ref[rt] != -INFINITY;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(fin && lm <= kPExp + kTau)) == 0, 1)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -659,29 +711,29 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
     } else {
       const float mx = max_x4(lm);               // row max, shifted
       const bool trig = !fin || mx > kPExp + kTau;
-      const float m_old = m_ref;
-      const float m_new = trig ? fmaxf(m_old, mx - sig) : m_old;
+      const float m_old = m_ref[rt];
+      const float m_new = trig ? fmaxf(m_old, mx - sig[rt]) : m_old;
       const float mref = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m_old - mref);   // 0 when m_old = -inf
-      const float delta = sig + mref - kPExp;
+      const float delta = sig[rt] + mref - kPExp;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s0[i] = fast_exp2(s0[i] - delta);
         s1[i] = fast_exp2(s1[i] - delta);
       }
       if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-        l_run *= alpha;
+        l_run[rt] *= alpha;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] *= alpha;
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) zacc[gg] *= alpha;
+        for (int gg = 0; gg < NG; ++gg) zacc[rt][gg] *= alpha;
       }
-      m_ref = m_new;
-      sig = m_new == -INFINITY ? 0.f : kPExp - m_new;
-      refresh();
+      m_ref[rt] = m_new;
+      sig[rt] = m_new == -INFINITY ? 0.f : kPExp - m_new;
+      refresh(rt);
     }
-    l_run += ((s0[0] + s1[0]) + (s0[1] + s1[1])) +
-             ((s0[2] + s1[2]) + (s0[3] + s1[3]));
+    l_run[rt] += ((s0[0] + s1[0]) + (s0[1] + s1[1])) +
+                 ((s0[2] + s1[2]) + (s0[3] + s1[3]));
   };
 
   // ---- one quantized 32-token tile from LDS
@@ -715,28 +767,31 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
         ak[st][ks] = u4v{r[0], r[1], r[2], r[3]};
       }
     }
-    f4v sc[2];
+    f4v sc[2][NRT];
     scores(sc, ak);
-    softmax(sc[0], sc[1]);
     // value scale pairs (tokens 4gq+i, 16+4gq+i; [i][group]) and zero pairs
     unsigned sz[8 * NG];
     lds_read<4 * NG>(tb + C::O_VSZ + 16 * NG * gq, sz);
     lds_read<4 * NG>(tb + C::O_VSZ + 16 * NG * gq + 64 * NG, sz + 4 * NG);
-    unsigned pp[4];
+    u4v bp[NRT][NG];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pp[i] = pack2(sc[0][i], sc[1][i]);
-    u4v bp[NG];
+    for (int rt = 0; rt < NRT; ++rt) {
+      softmax(rt, sc[0][rt], sc[1][rt]);
+      unsigned pp[4];
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      float z = zacc[gg];
+      for (int i = 0; i < 4; ++i) pp[i] = pack2(sc[0][rt][i], sc[1][rt][i]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const unsigned q = hmul2(pp[i], sz[i * NG + gg]);
-        bp[gg][i] = q;
-        z = dot2(pp[i], sz[4 * NG + i * NG + gg], z);
-        if constexpr (!C::LOW) z = dot2(q, C::NEG, z);   // code offset
+      for (int gg = 0; gg < NG; ++gg) {
+        float z = zacc[rt][gg];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const unsigned q = hmul2(pp[i], sz[i * NG + gg]);
+          bp[rt][gg][i] = q;
+          z = dot2(pp[i], sz[4 * NG + i * NG + gg], z);
+          if constexpr (!C::LOW) z = dot2(q, C::NEG, z);   // code offset
+        }
+        zacc[rt][gg] = z;
       }
-      zacc[gg] = z;
     }
     unsigned vh[C::NDV], vl[C::TWO ? C::NDV : 1];
     lds_read<C::NDV>(tb + C::O_VH + lane * (D * C::W / 16), vh);
@@ -754,7 +809,10 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
         for (int j = 0; j < 4; ++j)
           r[j] = declow<C::W>(vh[mt / PER], 4 * (mt % PER) + j, dk);
       }
-      acc[mt] = mfma16(u4v{r[0], r[1], r[2], r[3]}, bp[mt / (MT / NG)], acc[mt]);
+      const u4v av = u4v{r[0], r[1], r[2], r[3]};
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+        acc[rt][mt] = mfma16(av, bp[rt][mt / (MT / NG)], acc[rt][mt]);
     }
   };
 
@@ -773,21 +831,25 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
       for (int ks = 0; ks < KS; ++ks)
         ak[st][ks] = u4v{kd[4 * ks], kd[4 * ks + 1], kd[4 * ks + 2], kd[4 * ks + 3]};
     }
-    f4v sc[2];
+    f4v sc[2][NRT];
     scores(sc, ak);
     // causal / validity mask: row sees positions <= L - T + t(row)
     const int p0 = (int)a.n_q + kTile * r;
-    const int lim = row < a.rows ? L - a.T + row / a.gs : L - 1;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int row = row_of(rt);
+      const int lim = row < a.rows ? L - a.T + row / a.gs : L - 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = p0 + 16 * st + 4 * gq + i;
-        sc[st][i] = pos <= lim ? sc[st][i] : -INFINITY;
-      }
-    softmax(sc[0], sc[1]);
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bpres[i] = pack2(sc[0][i], sc[1][i]);
+        for (int i = 0; i < 4; ++i) {
+          const int pos = p0 + 16 * st + 4 * gq + i;
+          sc[st][rt][i] = pos <= lim ? sc[st][rt][i] : -INFINITY;
+        }
+      softmax(rt, sc[0][rt], sc[1][rt]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bpres[rt][i] = pack2(sc[0][rt][i], sc[1][rt][i]);
+    }
   };
 
   // ---- ring tile r, second unit: fp16 V (token-permuted) -> O
@@ -805,10 +867,12 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      acc[mt] = mfma16(
-          u4v{vd[4 * mt], vd[4 * mt + 1], vd[4 * mt + 2], vd[4 * mt + 3]},
-          bpres, acc[mt]);
+    for (int mt = 0; mt < MT; ++mt) {
+      const u4v av = u4v{vd[4 * mt], vd[4 * mt + 1], vd[4 * mt + 2], vd[4 * mt + 3]};
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+        acc[rt][mt] = mfma16(av, bpres[rt], acc[rt][mt]);
+    }
   };
 
   // ---- the unit loops, ring tiles first (K and V unit pairs), then the
@@ -882,6 +946,8 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
       n_ring = nr > n_ring ? nr : n_ring;
       n_quant = nq > n_quant ? nq : n_quant;
     }
+    n_ring = __builtin_amdgcn_readfirstlane(n_ring);
+    n_quant = __builtin_amdgcn_readfirstlane(n_quant);
     auto sync_step = [&](int u, bool active) __attribute__((always_inline)) {
       if (loader && active) {
         int pending = 0;
@@ -944,42 +1010,54 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
 
   // ---- per-wave finish: full-row l, zero-point term folded into o; all
   // sums carry the 2^kPExp of the probabilities
-  l_run = sum_x4(l_run) * kOScale;
 #pragma unroll
-  for (int gg = 0; gg < NG; ++gg) zacc[gg] = sum_x4(zacc[gg]) * kOScale;
+  for (int rt = 0; rt < NRT; ++rt) {
+    l_run[rt] = sum_x4(l_run[rt]) * kOScale;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    acc[mt] = acc[mt] * kOScale + zacc[mt / (MT / NG)];
+    for (int gg = 0; gg < NG; ++gg) zacc[rt][gg] = sum_x4(zacc[rt][gg]) * kOScale;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      acc[rt][mt] = acc[rt][mt] * kOScale + zacc[rt][mt / (MT / NG)];
+  }
 
   // ---- merge the NS streams (per row tile) through LDS, halving each step
   // slab rows padded by 4 floats: the 16 rows of a put/take land in
   // different banks
-  constexpr int DP = D + 4;
+  constexpr int DP = C::DP;
   float* s_slab = (float*)smem;
-  float* s_ml = s_slab + (NS / 2) * NH * 16 * DP;
+  float* s_ml = s_slab + (NS / 2) * RTT * 16 * DP;
   auto put = [&](int slot_m) __attribute__((always_inline)) {
-    float* o = s_slab + (slot_m * NH + h) * 16 * DP;
-    float* ml = s_ml + (slot_m * NH + h) * 32;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      *(f4v*)(o + l16 * DP + 16 * mt + 4 * gq) = acc[mt];
-    if (gq == 0) {
-      ml[l16] = m_ref;
-      ml[16 + l16] = l_run;
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int tt = slot_m * RTT + h * NRT + rt;
+      float* o = s_slab + tt * 16 * DP;
+      float* ml = s_ml + tt * 32;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        *(f4v*)(o + l16 * DP + 16 * mt + 4 * gq) = acc[rt][mt];
+      if (gq == 0) {
+        ml[l16] = m_ref[rt];
+        ml[16 + l16] = l_run[rt];
+      }
     }
   };
   auto take = [&](int slot_m) __attribute__((always_inline)) {
-    const float* o = s_slab + (slot_m * NH + h) * 16 * DP;
-    const float* ml = s_ml + (slot_m * NH + h) * 32;
-    const float mo = ml[l16], lo = ml[16 + l16];
-    const float M = fmaxf(m_ref, mo);
-    const float fa = M == -INFINITY ? 0.f : fast_exp2(m_ref - M);
-    const float fb = M == -INFINITY ? 0.f : fast_exp2(mo - M);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      acc[mt] = acc[mt] * fa + *(const f4v*)(o + l16 * DP + 16 * mt + 4 * gq) * fb;
-    l_run = l_run * fa + lo * fb;
-    m_ref = M;
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int tt = slot_m * RTT + h * NRT + rt;
+      const float* o = s_slab + tt * 16 * DP;
+      const float* ml = s_ml + tt * 32;
+      const float mo = ml[l16], lo = ml[16 + l16];
+      const float M = fmaxf(m_ref[rt], mo);
+      const float fa = M == -INFINITY ? 0.f : fast_exp2(m_ref[rt] - M);
+      const float fb = M == -INFINITY ? 0.f : fast_exp2(mo - M);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[rt][mt] = acc[rt][mt] * fa +
+                      *(const f4v*)(o + l16 * DP + 16 * mt + 4 * gq) * fb;
+      l_run[rt] = l_run[rt] * fa + lo * fb;
+      m_ref[rt] = M;
+    }
   };
   __syncthreads();   // every stream is done with its stages
 #pragma unroll
@@ -990,16 +1068,23 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
     __syncthreads();
   }
 
-  // ---- workgroup partial: o[RP][D], m[RP], l[RP]
+  // ---- workgroup partial: o[RP][D], m[RP], l[RP] (rows past `rows` are
+  // never read by the merge and are not written)
   if (strm == 0) {
     const int64_t pstride = (int64_t)RP * (D + 2);
     float* po = a.ws + (blk * a.s_alloc + split) * pstride;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      *(f4v*)(po + row * D + 16 * mt + 4 * gq) = acc[mt];
-    if (gq == 0) {
-      po[RP * D + row] = m_ref;
-      po[RP * D + RP + row] = l_run;
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int row = row_of(rt);
+      if (16 * (h * NRT + rt) < a.rows) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          *(f4v*)(po + row * D + 16 * mt + 4 * gq) = acc[rt][mt];
+        if (gq == 0) {
+          po[RP * D + row] = m_ref[rt];
+          po[RP * D + RP + row] = l_run[rt];
+        }
+      }
     }
   }
 }
@@ -1007,39 +1092,39 @@ __global__ void __launch_bounds__(512) attn_kernel(const AttnArgs a) {
 constexpr int kMaxDevices = 64;
 
 // Workgroups of one instantiation resident per CU on `dev` (0 if unknown).
-template <int PATH, int D, int NG, bool PAIR>
+template <int PATH, int D, int NG, int NRT, bool PAIR>
 int occupancy(int dev) {
-  using C = Cfg<PATH, D, NG, PAIR>;
+  using C = Cfg<PATH, D, NG, NRT, PAIR>;
   static int cache[kMaxDevices];   // 0 = not queried yet
   if (dev < 0 || dev >= kMaxDevices) return 0;
   if (cache[dev] == 0) {
     hipError_t e = hipFuncSetAttribute(
-        (const void*)attn_kernel<PATH, D, NG, PAIR>,
+        (const void*)attn_kernel<PATH, D, NG, NRT, PAIR>,
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return 0;
     int n = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &n, (const void*)attn_kernel<PATH, D, NG, PAIR>, C::NW * kWave, C::LDS);
+        &n, (const void*)attn_kernel<PATH, D, NG, NRT, PAIR>, C::NW * kWave, C::LDS);
     if (e != hipSuccess || n < 1) return 0;
     cache[dev] = n;
   }
   return cache[dev];
 }
 
-template <int PATH, int D, int NG, bool PAIR>
+template <int PATH, int D, int NG, int NRT, bool PAIR>
 hipError_t go(AttnArgs a, hipStream_t s) {
-  using C = Cfg<PATH, D, NG, PAIR>;
+  using C = Cfg<PATH, D, NG, NRT, PAIR>;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const int occ = occupancy<PATH, D, NG, PAIR>(dev);
+  const int occ = occupancy<PATH, D, NG, NRT, PAIR>(dev);
   if (occ < 1) return hipErrorInvalidConfiguration;
   const int64_t nb = (int64_t)a.g.B * a.g.Hkv;
   const int64_t units = 2 * cdiv(a.n_r, kTile) + cdiv(a.n_q / kTile, C::TPU);
   a.S = plan_splits(nb, (int64_t)cus * occ, units, C::NS, a.s_alloc);
-  hipLaunchKernelGGL((attn_kernel<PATH, D, NG, PAIR>),
+  hipLaunchKernelGGL((attn_kernel<PATH, D, NG, NRT, PAIR>),
                      dim3((unsigned)(nb * a.S)), dim3(C::NW * kWave), C::LDS, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1048,19 +1133,22 @@ hipError_t go(AttnArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int PATH, int D, bool PAIR>
+template <int PATH, int D, int NRT, bool PAIR>
 hipError_t by_ng(const AttnArgs& a, hipStream_t s) {
   switch (a.g.d / a.g.Gv) {
-    case 1: return go<PATH, D, 1, PAIR>(a, s);
-    case 2: return go<PATH, D, 2, PAIR>(a, s);
-    case 4: return go<PATH, D, 4, PAIR>(a, s);
+    case 1: return go<PATH, D, 1, NRT, PAIR>(a, s);
+    case 2: return go<PATH, D, 2, NRT, PAIR>(a, s);
+    case 4: return go<PATH, D, 4, NRT, PAIR>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+// 17..32 rows: two waves share a stream, one row tile each (measured
+// faster than one wave holding both row tiles at one wave per SIMD).
 template <int PATH, int D>
 hipError_t by_rows(const AttnArgs& a, hipStream_t s) {
-  return a.rows_pad == 16 ? by_ng<PATH, D, false>(a, s) : by_ng<PATH, D, true>(a, s);
+  if (a.rows_pad == 16) return by_ng<PATH, D, 1, false>(a, s);
+  return by_ng<PATH, D, 1, true>(a, s);
 }
 
 }  // namespace
