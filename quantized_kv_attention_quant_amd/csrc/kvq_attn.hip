@@ -219,67 +219,11 @@ __device__ __forceinline__ void lds_read(const unsigned char* p, unsigned* o) {
   }
 }
 
-// ---- direct global -> LDS copies --------------------------------------------
-// One instruction moves 16 bytes per lane: lane l's bytes g + voff land at
-// LDS address M0 + 16 l.  The compiler does not see these loads (it would
-// wait for every pending one before any LDS read), so the copies are counted
-// by hand with s_waitcnt vmcnt; M0 is restored after each one.
-__device__ __forceinline__ void dma16(const void* gp, unsigned voff,
-                                      unsigned lds) {
-  // the base must sit in SGPRs: it is wave-uniform by construction.
-  // readfirstlane returns int: zero-extend each half (a sign-extended low
-  // half would set the upper address bits)
-  const uint64_t gi = (uint64_t)(uintptr_t)gp;
-  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)gi);
-  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(gi >> 32));
-  const uint64_t g = lo | (hi << 32);
-  unsigned save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(lds), "v"(voff), "s"(g)
-      : "memory");
-}
-
-constexpr int dma_count(int bytes) { return (bytes + 1023) / 1024; }
-
-// Copy BYTES (a multiple of 16) from g to LDS address lds: dma_count(BYTES)
-// instructions, the last one on the first (BYTES % 1024) / 16 lanes.
-template <int BYTES>
-__device__ __forceinline__ void dma(const unsigned char* g, unsigned lds,
-                                    unsigned lane16) {
-  static_assert(BYTES % 16 == 0, "16-byte pieces");
-#pragma unroll
-  for (int k = 0; k < BYTES / 1024; ++k) dma16(g + 1024 * k, lane16, lds + 1024 * k);
-  if constexpr (BYTES % 1024 != 0) {
-    constexpr int full = BYTES / 1024 * 1024;
-    if (lane16 < (unsigned)(BYTES % 1024)) dma16(g + full, lane16, lds + full);
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Wait until at most `pending` copies are outstanding, rounded down to one
-// of the counts K*A or K*B (K < ST); waiting for more than needed is safe.
-template <int A, int B, int K>
-__device__ __forceinline__ void wait_le(int pending) {
-  if constexpr (K == 0) {
-    wait_vm<0>();
-  } else {
-    constexpr int hi = K * A > K * B ? K * A : K * B;
-    constexpr int lo = K * A > K * B ? K * B : K * A;
-    if (pending >= hi) { wait_vm<hi>(); return; }
-    if (pending >= lo) { wait_vm<lo>(); return; }
-    wait_le<A, B, K - 1>(pending);
-  }
-}
+// Units move in 1 KB chunks: the NH waves of a stream load each chunk into
+// registers (16/NH bytes per lane, one coalesced load per wave) and write it
+// to the unit's LDS stage; a partial last chunk of a piece is loaded by the
+// lanes whose bytes fall inside it.
+constexpr int chunks_of(int bytes) { return (bytes + 1023) / 1024; }
 
 // Per-path geometry.  A wave owns NRT 16-row tiles of the block's rows.
 // SOLO streams (every wave its own run of units) carry NRT = 1 or 2 row
@@ -311,27 +255,27 @@ struct Cfg {
   static constexpr int O_KSZ = O_VSZ + VSZB;
   static constexpr int TILE = O_KSZ + KSZB;
   static constexpr int RESU = 64 * D;            // fp16 K or V of a ring tile
-  static constexpr int TPU = (RESU + TILE - 1) / TILE;
-  static constexpr int STAGE = TPU * TILE;
+  // 1 KB chunks: a ring unit, a quantized tile; tiles per unit so that a
+  // unit has about as many chunks as a ring unit
+  static constexpr int NIR = chunks_of(RESU);
   static constexpr int NI_TILE =
-      (TWO ? 4 : 2) * dma_count(PL) + dma_count(VSZB) + dma_count(KSZB);
+      (TWO ? 4 : 2) * chunks_of(PL) + chunks_of(VSZB) + chunks_of(KSZB);
+  static constexpr int TPU = NIR / NI_TILE > 1 ? NIR / NI_TILE : 1;
   static constexpr int NIQ = TPU * NI_TILE;
-  static constexpr int NIR = dma_count(RESU);
+  static constexpr int NI = NIQ > NIR ? NIQ : NIR;
+  static constexpr int STAGE = TPU * TILE > RESU ? TPU * TILE : RESU;
   static constexpr int QB = RP * D * 2;          // staged q rows (fp16)
-  // waves per workgroup: 8 (two per SIMD) unless eight solo streams of two
-  // stages do not fit the LDS, or a wave holds two row tiles (its state
-  // then needs more than the 256 registers of two waves per SIMD)
-  static constexpr int NW =
-      NRT == 1 && (PAIR || 16 * STAGE + QB <= kLdsBytes) ? 8 : 4;
+  // waves per workgroup: 8 (two per SIMD) unless a wave holds two row
+  // tiles (its state then needs more than the 256 registers of two waves
+  // per SIMD)
+  static constexpr int NW = NRT == 1 ? 8 : 4;
   static constexpr int NS = NW / NH;             // unit streams per workgroup
-  static constexpr int ST0 = (kLdsBytes - QB) / (NS * STAGE);
-  static constexpr int ST = ST0 > 4 ? 4 : ST0;
-  static constexpr int LDS = NS * ST * STAGE + QB;
+  // one LDS stage per wave: a wave writes and reads its own stage, in order
+  static constexpr int LDS = NW * STAGE + QB;
   static constexpr int DP = D + 4;               // merge slab row (floats)
   static constexpr int MERGE = (NS / 2) * RTT * 16 * (DP + 2) * 4;
-  static_assert(ST >= (PAIR ? 3 : 2), "stages per stream");
-  static_assert((ST - 1) * (NIQ > NIR ? NIQ : NIR) <= 63, "vmcnt range");
-  static_assert(MERGE <= NS * ST * STAGE, "merge slabs fit the stage area");
+  static_assert(LDS <= kLdsBytes, "LDS");
+  static_assert(MERGE <= NW * STAGE, "merge slabs fit the stage area");
 };
 
 // Merge kernel, one workgroup per (block, row): combines the row's S split
@@ -416,7 +360,7 @@ template <int PATH, int D, int NG, int NRT, bool PAIR>
 __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     attn_kernel(const AttnArgs a) {
   using C = Cfg<PATH, D, NG, NRT, PAIR>;
-  constexpr int KS = C::KS, MT = C::MT, ST = C::ST, NS = C::NS, RTT = C::RTT;
+  constexpr int KS = C::KS, MT = C::MT, NS = C::NS, RTT = C::RTT;
   constexpr int RP = C::RP;
   constexpr int NT = C::NW * kWave;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -430,13 +374,11 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int strm = PAIR ? wave >> 1 : wave;      // stream in the workgroup
   const int h = PAIR ? wave & 1 : 0;             // row tile of this wave
-  const bool loader = h == 0;                    // issues the stream's copies
   const int lane = tid % kWave, l16 = lane & 15, gq = lane >> 4;
   // this lane's row in row tile rt of the wave
   auto row_of = [&](int rt) __attribute__((always_inline)) {
     return l16 + 16 * (h * NRT + rt);
   };
-  const unsigned lane16 = 16u * lane;
   const int L = (int)(a.n_q + a.n_r);
 
   // ---- the stream's run of units (32-bit: L_max <= 2^24 tokens)
@@ -454,9 +396,8 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   const int u0 = __builtin_amdgcn_readfirstlane(bound(c0s + strm));
   const int u1 = __builtin_amdgcn_readfirstlane(bound(c0s + strm + 1));
 
-  unsigned char* stages = smem + strm * ST * C::STAGE;
-  const unsigned lds_stages = (unsigned)(uintptr_t)stages;
-  __half* s_q = (__half*)(smem + NS * ST * C::STAGE);
+  unsigned char* stages = smem + wave * C::STAGE;
+  __half* s_q = (__half*)(smem + C::NW * C::STAGE);
 
   const uint8_t* kh_base = a.p.k_hi + blk * g.k_block_bytes;
   const uint8_t* kl_base = C::TWO ? a.p.k_lo + blk * g.k_block_bytes : nullptr;
@@ -469,78 +410,118 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   const int nq_mod = (int)(a.n_q % g.ring);
   const int tiles_per_group = g.G / kTile;
 
-  auto issue = [&](int u, int slot) __attribute__((always_inline)) {
+  // ---- staged loads of a unit: fetch loads the unit's chunks into stg
+  // (16 bytes per lane, one coalesced instruction per 1 KB chunk), commit
+  // writes them to this wave's stage (the compiler waits for the loads
+  // there).  Every path of fetch loads every stg entry (lanes past a partial
+  // chunk and chunks past a ring unit re-read valid bytes, at addresses no
+  // other load uses): a register left unloaded on one path, or a load merged
+  // with an identical one, would be filled by a copy, and the copy would
+  // wait for the loads just issued.
+  const unsigned lofs = 16u * lane;
+  // Stage layout: within each 1 KB chunk, the 16-byte pieces of the code
+  // planes and of the ring tiles are XOR-permuted so that the compute's
+  // LDS reads (16 bytes per lane, rows of 64, 256 or 128 bytes apart) fall
+  // in distinct banks; the writes of a chunk stay a permutation of it.
+  // Piece p = 64 k + l of a chunk is written by lane l; *_pat is its
+  // physical piece within the chunk (identity where the geometry differs).
+  constexpr bool SWZ = D == 128 && C::W == 4;   // code planes: 64-byte rows
+  constexpr bool SWZR = D == 128;               // ring tiles: 256-byte rows
+  const unsigned kpat = SWZ ? (lane & ~3u) | ((lane ^ (lane >> 3)) & 3u) : lane;
+  const unsigned vpat = SWZ ? (lane & ~1u) | ((lane ^ (lane >> 3)) & 1u) : lane;
+  const unsigned rkpat0 = SWZR ? (lane & ~15u) | ((lane ^ (lane >> 4)) & 15u) : lane;
+  const unsigned rkpat1 = SWZR ? (lane & ~15u) | ((lane ^ (4u + (lane >> 4))) & 15u) : lane;
+  const unsigned rvpat = SWZR ? (lane & ~7u) | ((lane ^ (lane >> 3)) & 7u) : lane;
+  u4v stg[C::NI];
+  // may_ring = false where u is known to be a quantized unit: one load
+  // path, so the buffer registers need no merging copies
+  auto fetch = [&](int u, bool may_ring) __attribute__((always_inline)) {
     u = __builtin_amdgcn_readfirstlane(u);          // keep the address math scalar
-    const unsigned ld = lds_stages + slot * C::STAGE;
-    if (u < nres) {
+    if (may_ring && u < nres) {
       int slot0 = nq_mod + kTile * (u >> 1);
       slot0 = slot0 >= g.ring ? slot0 - g.ring : slot0;
       const uint8_t* src = ((u & 1) ? vres_base : kres_base) + (unsigned)slot0 * (D * 2);
-      dma<C::RESU>(src, ld, lane16);
+#pragma unroll
+      for (int i = 0; i < C::NI; ++i)   // past NIR: re-reads at distinct addresses
+        stg[i] = *(const u4v*)(src + (i < C::NIR ? 1024 * i + lofs
+                                                 : 1024 * (i - C::NIR) + lofs + 16));
     } else {
       const int t0 = (u - nres) * C::TPU;
 #pragma unroll
       for (int j = 0; j < C::TPU; ++j) {
-        const int t = t0 + j;
-        if (t < nqt) {
-          const unsigned lt = ld + j * C::TILE;
-          const unsigned po = (unsigned)t * C::PL;
-          dma<C::PL>(kh_base + po, lt + C::O_KH, lane16);
-          if constexpr (C::TWO) dma<C::PL>(kl_base + po, lt + C::O_KL, lane16);
-          dma<C::PL>(vh_base + po, lt + C::O_VH, lane16);
-          if constexpr (C::TWO) dma<C::PL>(vl_base + po, lt + C::O_VL, lane16);
-          dma<C::VSZB>(vsz_base + (unsigned)t * C::VSZB, lt + C::O_VSZ, lane16);
-          dma<C::KSZB>(ksz_base + (unsigned)(t / tiles_per_group) * C::KSZB,
-                       lt + C::O_KSZ, lane16);
-        }
+        int t = t0 + j < nqt ? t0 + j : nqt - 1;
+        t = t > 0 ? t : 0;
+        const unsigned po = (unsigned)t * C::PL;
+        const uint8_t* src[6] = {kh_base + po, kl_base + po, vh_base + po, vl_base + po,
+                                 vsz_base + (unsigned)t * C::VSZB,
+                                 ksz_base + (unsigned)(t / tiles_per_group) * C::KSZB};
+        constexpr int bytes[6] = {C::PL, C::TWO ? C::PL : 0, C::PL, C::TWO ? C::PL : 0,
+                                  C::VSZB, C::KSZB};
+        int i = j * C::NI_TILE;
+#pragma unroll
+        for (int pc = 0; pc < 6; ++pc)
+#pragma unroll
+          for (int k = 0; k < chunks_of(bytes[pc]); ++k, ++i) {
+            const int rem = bytes[pc] - 1024 * k;
+            const unsigned o = rem >= 1024 || lofs < (unsigned)rem ? lofs : 0u;
+            stg[i] = *(const u4v*)(src[pc] + 1024 * k + o);
+          }
       }
     }
   };
-  auto count = [&](int u) __attribute__((always_inline)) -> int {
-    if (u < nres) return C::NIR;
-    const int left = nqt - (u - nres) * C::TPU;
-    return (left < C::TPU ? left : C::TPU) * C::NI_TILE;
+  auto commit = [&](int u) __attribute__((always_inline)) {
+    if (u < nres) {
+      const unsigned pk = 16u * ((u & 1) ? rvpat : rkpat0);
+      const unsigned pk1 = 16u * ((u & 1) ? rvpat : rkpat1);
+#pragma unroll
+      for (int i = 0; i < C::NIR; ++i)
+        *(u4v*)(stages + 1024 * i + ((i & 1) ? pk1 : pk)) = stg[i];
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::TPU; ++j) {
+        constexpr int bytes[6] = {C::PL, C::TWO ? C::PL : 0, C::PL, C::TWO ? C::PL : 0,
+                                  C::VSZB, C::KSZB};
+        constexpr int offs[6] = {C::O_KH, C::O_KL, C::O_VH, C::O_VL, C::O_VSZ, C::O_KSZ};
+        int i = j * C::NI_TILE;
+#pragma unroll
+        for (int pc = 0; pc < 6; ++pc)
+#pragma unroll
+          for (int k = 0; k < chunks_of(bytes[pc]); ++k, ++i) {
+            const int rem = bytes[pc] - 1024 * k;
+            const unsigned o = pc < 2 ? 16u * kpat : pc < 4 ? 16u * vpat : lofs;
+            if (rem >= 1024 || lofs < (unsigned)rem)
+              *(u4v*)(stages + j * C::TILE + offs[pc] + 1024 * k + o) = stg[i];
+          }
+      }
+    }
   };
 
-  // ---- stage the query rows and prefetch the first ST-1 units.  The rows
-  // come in with the same direct copies (16-byte chunk k of s_q from row
-  // k / (D/8)); copy instruction i is issued by wave i % NW before its units,
-  // so waiting for its units' count leaves the query rows landed.
-  const int q_chunks = a.rows * (D / 8);
-  int my_q = 0;
-  for (int i = wave; i * kWave < q_chunks; i += C::NW) {
-    const int k = i * kWave + lane;
-    const unsigned ldq = __builtin_amdgcn_readfirstlane(
-        (unsigned)(uintptr_t)s_q + 16u * i * kWave);
-    if (k < q_chunks) {
-      const int r = k / (D / 8), c8 = k % (D / 8);
-      const int t = r / a.gs, hl = r % a.gs;
-      const unsigned off = (unsigned)((((int64_t)b * a.T + t) * a.Hq +
-                                       kvh * a.gs + hl) * D + 8 * c8) * 2u;
-      dma16(a.q, off, ldq);
+  // ---- stage the query rows (zero past `rows`); the loads go out before
+  // the first unit's, so waiting for them leaves that unit in flight
+  {
+    constexpr int QPT = (RP * (D / 8) + NT - 1) / NT;   // 16-byte chunks per thread
+    const int q_chunks = a.rows * (D / 8);
+    u4v qv[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int k = tid + i * NT;
+      qv[i] = u4v{0u, 0u, 0u, 0u};
+      if (k < q_chunks) {
+        const int r = k / (D / 8), c8 = k % (D / 8);
+        const int t = r / a.gs, hl = r % a.gs;
+        qv[i] = *(const u4v*)(a.q + (((int64_t)b * a.T + t) * a.Hq + kvh * a.gs + hl) * D +
+                              8 * c8);
+      }
     }
-    ++my_q;
-  }
-  // Only the first unit goes out with the query rows: the whole grid's
-  // first requests then land sooner, the rest of the prefetch follows once
-  // the rows are in.
-  int slot_in = 0, pro = 0;
-  if (loader && u0 < u1) {
-    issue(u0, slot_in);
-    pro = count(u0);
-    slot_in = 1;
-  }
-  for (int k = q_chunks + tid; k < RP * (D / 8); k += NT)   // padded rows
-    *(uint4*)(s_q + 8 * k) = make_uint4(0u, 0u, 0u, 0u);
-  if (my_q) wait_le<C::NIQ, C::NIR, 1>(pro);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  if (loader) {
-    for (int u = u0 + 1; u < u0 + ST - 1 && u < u1; ++u) {
-      issue(u, slot_in);
-      slot_in = slot_in + 1 == ST ? 0 : slot_in + 1;
+    if (u0 < u1) fetch(u0, true);
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int k = tid + i * NT;
+      if (k < RP * (D / 8)) *(u4v*)(s_q + 8 * k) = qv[i];
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
 
   // ---- per-wave state (NRT 16-row tiles)
@@ -747,7 +728,8 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     u4v ak[2][KS];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int ko = (l16 + 16 * st) * (D * C::W / 8) + gq * (D * C::W / 32);
+      const int ko = SWZ ? ((l16 + 16 * st) * 4 + (gq ^ ((l16 >> 1) & 3))) * 16
+                         : (l16 + 16 * st) * (D * C::W / 8) + gq * (D * C::W / 32);
       unsigned kh[C::NDK], kl[C::TWO ? C::NDK : 1];
       lds_read<C::NDK>(tb + C::O_KH + ko, kh);
       if constexpr (C::TWO) lds_read<C::NDK>(tb + C::O_KL + ko, kl);
@@ -794,8 +776,19 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
       }
     }
     unsigned vh[C::NDV], vl[C::TWO ? C::NDV : 1];
-    lds_read<C::NDV>(tb + C::O_VH + lane * (D * C::W / 16), vh);
-    if constexpr (C::TWO) lds_read<C::NDV>(tb + C::O_VL + lane * (D * C::W / 16), vl);
+    if constexpr (SWZ) {      // halves of lane l's 32 bytes, swapped when bit 2 of l is set
+      const int s0 = (lane >> 2) & 1;
+      const int v0 = (2 * lane + s0) * 16, v1 = (2 * lane + 1 - s0) * 16;
+      lds_read<4>(tb + C::O_VH + v0, vh);
+      lds_read<4>(tb + C::O_VH + v1, vh + 4);
+      if constexpr (C::TWO) {
+        lds_read<4>(tb + C::O_VL + v0, vl);
+        lds_read<4>(tb + C::O_VL + v1, vl + 4);
+      }
+    } else {
+      lds_read<C::NDV>(tb + C::O_VH + lane * (D * C::W / 16), vh);
+      if constexpr (C::TWO) lds_read<C::NDV>(tb + C::O_VL + lane * (D * C::W / 16), vl);
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       unsigned r[4];
@@ -826,7 +819,13 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       unsigned kd[D / 8];
-      lds_read<D / 8>(sb + ((l16 + 16 * st) * D + gq * (D / 4)) * 2, kd);
+      if constexpr (SWZR) {   // pieces gq*4 + j of row l16 + 16 st, XOR (row & 7)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          lds_read<4>(sb + ((l16 + 16 * st) * 16 + ((gq * 4 + j) ^ (l16 & 7))) * 16, kd + 4 * j);
+      } else {
+        lds_read<D / 8>(sb + ((l16 + 16 * st) * D + gq * (D / 4)) * 2, kd);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         ak[st][ks] = u4v{kd[4 * ks], kd[4 * ks + 1], kd[4 * ks + 2], kd[4 * ks + 3]};
@@ -855,7 +854,12 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   // ---- ring tile r, second unit: fp16 V (token-permuted) -> O
   auto ring_v = [&](const unsigned char* sb, int r) __attribute__((always_inline)) {
     unsigned vd[D / 4];
-    lds_read<D / 4>(sb + lane * D, vd);
+    if constexpr (SWZR) {     // pieces j of lane l's 128 bytes, XOR (l & 7)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lds_read<4>(sb + (8 * lane + (j ^ (lane & 7))) * 16, vd + 4 * j);
+    } else {
+      lds_read<D / 4>(sb + lane * D, vd);
+    }
     const int p0 = (int)a.n_q + kTile * r;
     if (p0 + kTile > L) {              // zero the slots past the context
 #pragma unroll
@@ -875,135 +879,46 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     }
   };
 
-  // ---- the unit loops, ring tiles first (K and V unit pairs), then the
-  // quantized prefix
-  int slot = 0;
-  auto next_slot = [](int x) __attribute__((always_inline)) { return x + 1 == ST ? 0 : x + 1; };
+  // ---- the unit loop, ring tiles first (K and V unit pairs), then the
+  // quantized prefix.  Per unit: its staged chunks go to the stage (the
+  // previous unit's reads of it were issued earlier, and LDS runs a wave's
+  // accesses in order), then the next unit is fetched while this one is
+  // computed.  No wave waits for another: the two waves of a 17..32-row
+  // stream each load the whole unit (the second read hits the cache).
+  auto step = [&](int u, bool quant_next) __attribute__((always_inline)) {
+    commit(u);
+    if (u + 1 < u1) fetch(u + 1, !quant_next);
+  };
   // may_build = false when every tile of the unit is known to belong to
-  // the current key group: the inner loops below then carry the B operands
-  // unchanged, so they stay in place in registers.
+  // the current key group: the inner loop below then carries the B
+  // operands unchanged, so they stay in place in registers.
   auto quant_unit = [&](int u, bool may_build) __attribute__((always_inline)) {
-    const unsigned char* sb = stages + slot * C::STAGE;
     const int t0 = (u - nres) * C::TPU;
 #pragma unroll
     for (int j = 0; j < C::TPU; ++j)
-      if (t0 + j < nqt) quant_tile(sb + j * C::TILE, t0 + j, may_build);
+      if (t0 + j < nqt) quant_tile(stages + j * C::TILE, t0 + j, may_build);
   };
   auto in_group = [&](int u) __attribute__((always_inline)) {
     const int t0 = (u - nres) * C::TPU;
     const int t1 = (t0 + C::TPU < nqt ? t0 + C::TPU : nqt) - 1;
     return t0 / tiles_per_group == cur_grp && t1 / tiles_per_group == cur_grp;
   };
-  if constexpr (!PAIR) {
-    // issue unit u + ST - 1 (into the slot of unit u - 1, computed by this
-    // wave), wait until unit u has landed, compute it
-    auto step = [&](int u) __attribute__((always_inline)) {
-      if (u + ST - 1 < u1) {
-        issue(u + ST - 1, slot_in);
-        slot_in = next_slot(slot_in);
-      }
-      int pending = 0;
-#pragma unroll
-      for (int k = 1; k < ST; ++k)
-        if (u + k < u1) pending += count(u + k);
-      wait_le<C::NIQ, C::NIR, ST - 1>(pending);
-    };
+  {
     int u = u0;
     const int ur = u1 < nres ? u1 : nres;
     for (; u < ur; u += 2) {
-      step(u);
-      ring_k(stages + slot * C::STAGE, u >> 1);
-      slot = next_slot(slot);
-      step(u + 1);
-      ring_v(stages + slot * C::STAGE, u >> 1);
-      slot = next_slot(slot);
+      step(u, false);
+      ring_k(stages, u >> 1);
+      step(u + 1, false);
+      ring_v(stages, u >> 1);
     }
     while (u < u1) {
-      step(u);
+      step(u, true);
       quant_unit(u, true);
-      slot = next_slot(slot);
       ++u;
       for (; u < u1 && in_group(u); ++u) {
-        step(u);
+        step(u, true);
         quant_unit(u, false);
-        slot = next_slot(slot);
-      }
-    }
-  } else {
-    // Two waves read every stage.  Per unit: the loader waits until unit u
-    // has landed, a workgroup barrier shows it to the partner and proves
-    // both are done with unit u - 1, then the loader refills that slot with
-    // unit u + ST - 1.  Every wave of the workgroup runs the same number of
-    // barriers: each phase iterates to the longest stream's count.
-    int n_ring = 0, n_quant = 0;
-#pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      const int a0 = bound(c0s + k), a1 = bound(c0s + k + 1);
-      const int r1 = a1 < nres ? a1 : nres;
-      const int nr = r1 > a0 ? r1 - a0 : 0;
-      const int q0 = a0 > nres ? a0 : nres;
-      const int nq = a1 > q0 ? a1 - q0 : 0;
-      n_ring = nr > n_ring ? nr : n_ring;
-      n_quant = nq > n_quant ? nq : n_quant;
-    }
-    n_ring = __builtin_amdgcn_readfirstlane(n_ring);
-    n_quant = __builtin_amdgcn_readfirstlane(n_quant);
-    auto sync_step = [&](int u, bool active) __attribute__((always_inline)) {
-      if (loader && active) {
-        int pending = 0;
-#pragma unroll
-        for (int k = 1; k + 1 < ST; ++k)
-          if (u + k < u1) pending += count(u + k);
-        wait_le<C::NIQ, C::NIR, ST - 2>(pending);
-      }
-      // plain s_barrier (a __syncthreads fence would also wait for every
-      // copy in flight); the asm statements keep LDS accesses on their side
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (loader && active && u + ST - 1 < u1) {
-        issue(u + ST - 1, slot_in);
-        slot_in = next_slot(slot_in);
-      }
-    };
-    const int ur = u1 < nres ? u1 : nres;
-    for (int i = 0; i < n_ring; i += 2) {
-      const int u = u0 + i;
-      const bool active = u < ur;
-      sync_step(u, active);
-      if (active) {
-        ring_k(stages + slot * C::STAGE, u >> 1);
-        slot = next_slot(slot);
-      }
-      sync_step(u + 1, active);
-      if (active) {
-        ring_v(stages + slot * C::STAGE, u >> 1);
-        slot = next_slot(slot);
-      }
-    }
-    // every iteration, outer or inner, runs exactly one barrier
-    const int uq = u0 > nres ? u0 : nres;
-    int i = 0;
-    while (i < n_quant) {
-      {
-        const int u = uq + i;
-        const bool active = u < u1;
-        sync_step(u, active);
-        if (active) {
-          quant_unit(u, true);
-          slot = next_slot(slot);
-        }
-        ++i;
-      }
-      for (; i < n_quant; ++i) {
-        const int u = uq + i;
-        const bool active = u < u1;
-        if (active && !in_group(u)) break;
-        sync_step(u, active);
-        if (active) {
-          quant_unit(u, false);
-          slot = next_slot(slot);
-        }
       }
     }
   }
