@@ -885,7 +885,16 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   // accesses in order), then the next unit is fetched while this one is
   // computed.  No wave waits for another: the two waves of a 17..32-row
   // stream each load the whole unit (the second read hits the cache).
+  // The two waves on a SIMD have about the same work, but the older one
+  // wins issue while both are ready: it would finish first and leave the
+  // other running alone.  Issue priority from the units left (3 down to 0
+  // over the last four) lets the wave behind catch up before the end.
   auto step = [&](int u, bool quant_next) __attribute__((always_inline)) {
+    const int rem = u1 - u;
+    if (rem >= 4) __builtin_amdgcn_s_setprio(3);
+    else if (rem == 3) __builtin_amdgcn_s_setprio(2);
+    else if (rem == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     commit(u);
     if (u + 1 < u1) fetch(u + 1, !quant_next);
   };
