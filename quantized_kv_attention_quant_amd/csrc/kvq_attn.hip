@@ -270,12 +270,13 @@ struct Cfg {
   // per SIMD)
   static constexpr int NW = NRT == 1 ? 8 : 4;
   static constexpr int NS = NW / NH;             // unit streams per workgroup
-  // one LDS stage per wave: a wave writes and reads its own stage, in order
-  static constexpr int LDS = NW * STAGE + QB;
+  // one LDS stage per wave: a wave writes and reads its own stage, in order;
+  // the stream-merge slabs reuse the stage area after the unit loop
   static constexpr int DP = D + 4;               // merge slab row (floats)
   static constexpr int MERGE = (NS / 2) * RTT * 16 * (DP + 2) * 4;
+  static constexpr int SAREA = NW * STAGE > MERGE ? NW * STAGE : MERGE;
+  static constexpr int LDS = SAREA + QB;
   static_assert(LDS <= kLdsBytes, "LDS");
-  static_assert(MERGE <= NW * STAGE, "merge slabs fit the stage area");
 };
 
 // Merge kernel, one workgroup per (block, row): combines the row's S split
@@ -397,7 +398,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   const int u1 = __builtin_amdgcn_readfirstlane(bound(c0s + strm + 1));
 
   unsigned char* stages = smem + wave * C::STAGE;
-  __half* s_q = (__half*)(smem + C::NW * C::STAGE);
+  __half* s_q = (__half*)(smem + C::SAREA);
 
   const uint8_t* kh_base = a.p.k_hi + blk * g.k_block_bytes;
   const uint8_t* kl_base = C::TWO ? a.p.k_lo + blk * g.k_block_bytes : nullptr;
