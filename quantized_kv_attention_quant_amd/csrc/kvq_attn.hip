@@ -11,13 +11,14 @@
 //   * a block's work is a sequence of units: two per 32-slot tile of the fp16
 //     ring (its K, then its V, 8 KB each at d = 128) followed by the
 //     quantized prefix in units of TPU 32-token tiles (codes, value
-//     scale/zero and the key scale/zero of the tile's group).  Every wave of
-//     the grid owns one contiguous run of units (a ring tile's two units never
-//     split), so waves never wait for each other inside the loop.
-//   * each wave streams its units through a private ring of ST stages in
-//     LDS with direct global->LDS loads (global_load_lds_dwordx4, issued
-//     ST-1 units ahead, counted with vmcnt), so the bytes in flight are not
-//     held in registers.
+//     scale/zero and the key scale/zero of the tile's group).  Every stream
+//     of the grid owns one contiguous run of units (a ring tile's two units
+//     never split); a stream is one wave (up to 16 rows) or two waves that
+//     take one 16-row tile each.  No wave waits for another inside the loop.
+//   * each wave loads its next unit into registers with plain coalesced
+//     16-byte loads while it computes the current one, then writes it to its
+//     own LDS stage (XOR-permuted 16-byte pieces, so the decode's strided
+//     reads are free of bank conflicts) and reads the operands from there.
 //   * per tile the wave computes S^T = K * Q'^T on MFMA (16x16x32 f16, two
 //     16-token subtiles x one or two 16-row tiles), runs the online softmax
 //     on the S^T accumulators in place and feeds P'^T straight back as the B
@@ -37,7 +38,7 @@
 //     row's reference (folded into the accumulator's initial value) and the
 //     reference is only raised when a score exceeds it by more than 2^3, so
 //     the common tile needs no cross-lane reduction and no rescale.
-//   * the waves of a workgroup merge through LDS and write one partial
+//   * the streams of a workgroup merge through LDS and write one partial
 //     (m, l, o) per workgroup.  A second launch, one workgroup per (block,
 //     row), merges that row's partials by log-sum-exp (fp16 output, natural-
 //     log LSE); the kernel boundary makes the partials visible.
@@ -353,7 +354,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
 }
 
 // Dynamic LDS of the split kernel:
-//   stages  [NS][ST][STAGE]   each stream's ring of units
+//   stages  [NW][STAGE]       each wave's unit stage
 //   s_q     fp16 [RP][D]      this block's query rows (zero past `rows`)
 // After the unit loop the stage area holds the stream-merge slabs
 //   slab float [NS/2][RTT][16][D+4], ml float [NS/2][RTT][2][16].
