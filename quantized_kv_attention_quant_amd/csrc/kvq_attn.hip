@@ -274,7 +274,7 @@ struct Cfg {
   // one LDS stage per wave: a wave writes and reads its own stage, in order;
   // the stream-merge slabs reuse the stage area after the unit loop
   static constexpr int DP = D + 4;               // merge slab row (floats)
-  static constexpr int MERGE = (NS / 2) * RTT * 16 * (DP + 2) * 4;
+  static constexpr int MERGE = (NS / 2) * RTT * 16 * (DP + 2) * 4;   // n - ceil(n/2) <= NS/2
   static constexpr int SAREA = NW * STAGE > MERGE ? NW * STAGE : MERGE;
   static constexpr int LDS = SAREA + QB;
   static_assert(LDS <= kLdsBytes, "LDS");
@@ -434,6 +434,13 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   const unsigned rkpat0 = SWZR ? (lane & ~15u) | ((lane ^ (lane >> 4)) & 15u) : lane;
   const unsigned rkpat1 = SWZR ? (lane & ~15u) | ((lane ^ (4u + (lane >> 4))) & 15u) : lane;
   const unsigned rvpat = SWZR ? (lane & ~7u) | ((lane ^ (lane >> 3)) & 7u) : lane;
+  // 4-bit planes at d = 128, one tile per unit: chunk k of a key plane is
+  // subtile k (16 tokens x 64 bytes), and lane (l16, gq) loads the 16 bytes
+  // it feeds to the score MFMA straight from memory (still one coalesced
+  // 1 KB per instruction).  The key codes then skip the stage; the tile's
+  // keys are decoded from the buffer before the next unit is fetched.
+  constexpr bool DIRECTK = SWZ && C::TPU == 1;
+  const unsigned kdir = 64u * (lane & 15u) + 16u * (lane >> 4);
   u4v stg[C::NI];
   // may_ring = false where u is known to be a quantized unit: one load
   // path, so the buffer registers need no merging copies
@@ -465,7 +472,8 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
 #pragma unroll
           for (int k = 0; k < chunks_of(bytes[pc]); ++k, ++i) {
             const int rem = bytes[pc] - 1024 * k;
-            const unsigned o = rem >= 1024 || lofs < (unsigned)rem ? lofs : 0u;
+            const unsigned o = DIRECTK && pc < 2 ? kdir
+                               : rem >= 1024 || lofs < (unsigned)rem ? lofs : 0u;
             stg[i] = *(const u4v*)(src[pc] + 1024 * k + o);
           }
       }
@@ -491,7 +499,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
           for (int k = 0; k < chunks_of(bytes[pc]); ++k, ++i) {
             const int rem = bytes[pc] - 1024 * k;
             const unsigned o = pc < 2 ? 16u * kpat : pc < 4 ? 16u * vpat : lofs;
-            if (rem >= 1024 || lofs < (unsigned)rem)
+            if (!(DIRECTK && pc < 2) && (rem >= 1024 || lofs < (unsigned)rem))
               *(u4v*)(stages + j * C::TILE + offs[pc] + 1024 * k + o) = stg[i];
           }
       }
@@ -558,7 +566,8 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   };
   constexpr int DAB = C::W == 4 ? 4 : C::W == 2 ? 8 : 16;   // cB - cA
   // With one row tile, q * c0 of those channels stays in registers for the
-  // whole run; with two it is re-read from LDS per key group (registers).
+  // whole run (measured faster than re-reading it from LDS per key group);
+  // with two it is re-read (registers).
   constexpr bool QC = NRT == 1;
   float qcA[QC ? KS : 1][4], qcB[QC ? KS : 1][4];
   auto load_qc = [&](int rt, int ks, float* fa, float* fb)
@@ -720,21 +729,25 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   };
 
   // ---- one quantized 32-token tile from LDS
-  auto quant_tile = [&](const unsigned char* tb, int t, bool may_build)
+  auto quant_tile = [&](const unsigned char* tb, int t, bool may_build, int u)
       __attribute__((always_inline)) {
-    const int grp = t / tiles_per_group;
-    if (may_build && grp != cur_grp) {
-      build_quant(tb + C::O_KSZ);
-      cur_grp = grp;
-    }
     u4v ak[2][KS];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int ko = SWZ ? ((l16 + 16 * st) * 4 + (gq ^ ((l16 >> 1) & 3))) * 16
                          : (l16 + 16 * st) * (D * C::W / 8) + gq * (D * C::W / 32);
       unsigned kh[C::NDK], kl[C::TWO ? C::NDK : 1];
-      lds_read<C::NDK>(tb + C::O_KH + ko, kh);
-      if constexpr (C::TWO) lds_read<C::NDK>(tb + C::O_KL + ko, kl);
+      if constexpr (DIRECTK) {
+        static_assert(C::NDK == 4, "one dword quad per subtile");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          kh[k] = stg[st][k];
+          if constexpr (C::TWO) kl[k] = stg[2 + st][k];
+        }
+      } else {
+        lds_read<C::NDK>(tb + C::O_KH + ko, kh);
+        if constexpr (C::TWO) lds_read<C::NDK>(tb + C::O_KL + ko, kl);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         unsigned r[4];
@@ -750,6 +763,14 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
         }
         ak[st][ks] = u4v{r[0], r[1], r[2], r[3]};
       }
+    }
+    if constexpr (DIRECTK) {
+      if (u + 1 < u1) fetch(u + 1, false);   // the buffer is free now
+    }
+    const int grp = t / tiles_per_group;
+    if (may_build && grp != cur_grp) {
+      build_quant(tb + C::O_KSZ);
+      cur_grp = grp;
     }
     f4v sc[2][NRT];
     scores(sc, ak);
@@ -898,7 +919,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     else if (rem == 2) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
     commit(u);
-    if (u + 1 < u1) fetch(u + 1, !quant_next);
+    if (!(DIRECTK && u >= nres) && u + 1 < u1) fetch(u + 1, !quant_next);
   };
   // may_build = false when every tile of the unit is known to belong to
   // the current key group: the inner loop below then carries the B
@@ -907,7 +928,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     const int t0 = (u - nres) * C::TPU;
 #pragma unroll
     for (int j = 0; j < C::TPU; ++j)
-      if (t0 + j < nqt) quant_tile(stages + j * C::TILE, t0 + j, may_build);
+      if (t0 + j < nqt) quant_tile(stages + j * C::TILE, t0 + j, may_build, u);
   };
   auto in_group = [&](int u) __attribute__((always_inline)) {
     const int t0 = (u - nres) * C::TPU;
@@ -986,11 +1007,14 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     }
   };
   __syncthreads();   // every stream is done with its stages
+  // halving steps over n live streams: streams [h, n) hand their state to
+  // streams [0, n - h), h = ceil(n / 2)
 #pragma unroll
-  for (int half = NS / 2; half >= 1; half /= 2) {
-    if (strm >= half && strm < 2 * half) put(strm - half);
+  for (int n = NS; n > 1; n = (n + 1) / 2) {
+    const int hh = (n + 1) / 2;
+    if (strm >= hh && strm < n) put(strm - hh);
     __syncthreads();
-    if (strm < half) take(strm);
+    if (strm < n - hh) take(strm);
     __syncthreads();
   }
 
