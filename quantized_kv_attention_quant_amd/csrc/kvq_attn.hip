@@ -444,6 +444,47 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   u4v stg[C::NI];
   // may_ring = false where u is known to be a quantized unit: one load
   // path, so the buffer registers need no merging copies
+  // Quantized tile pieces: 0/1 key planes, 2/3 value planes, 4 value
+  // scales, 5 key scales; stg index of the first chunk of each piece.
+  constexpr int kBytes[6] = {C::PL, C::TWO ? C::PL : 0, C::PL, C::TWO ? C::PL : 0,
+                             C::VSZB, C::KSZB};
+  constexpr int kFirst[6] = {0, chunks_of(kBytes[0]),
+                             chunks_of(kBytes[0]) + chunks_of(kBytes[1]),
+                             chunks_of(kBytes[0]) + chunks_of(kBytes[1]) + chunks_of(kBytes[2]),
+                             C::NI_TILE - chunks_of(C::VSZB) - chunks_of(C::KSZB),
+                             C::NI_TILE - chunks_of(C::KSZB)};
+  // parts: 1 = keys and scales, 2 = values (with DIRECTK the values too come
+  // straight to the registers, lane l holding its 32 bytes of each plane)
+  auto fetch_quant = [&](int u, int parts) __attribute__((always_inline)) {
+    const int t0 = (u - nres) * C::TPU;
+#pragma unroll
+    for (int j = 0; j < C::TPU; ++j) {
+      int t = t0 + j < nqt ? t0 + j : nqt - 1;
+      t = t > 0 ? t : 0;
+      const unsigned po = (unsigned)t * C::PL;
+      const uint8_t* src[6] = {kh_base + po, kl_base + po, vh_base + po, vl_base + po,
+                               vsz_base + (unsigned)t * C::VSZB,
+                               ksz_base + (unsigned)(t / tiles_per_group) * C::KSZB};
+      constexpr int order[6] = {0, 1, 4, 5, 2, 3};   // keys and scales first
+#pragma unroll
+      for (int oi = 0; oi < 6; ++oi) {
+        const int pc = order[oi];
+        if (!(parts & (pc == 2 || pc == 3 ? 2 : 1))) continue;
+#pragma unroll
+        for (int k = 0; k < chunks_of(kBytes[pc]); ++k) {
+          const int i = j * C::NI_TILE + kFirst[pc] + k;
+          const int rem = kBytes[pc] - 1024 * k;
+          if (DIRECTK && (pc == 2 || pc == 3)) {
+            stg[i] = *(const u4v*)(src[pc] + 32u * lane + 16 * k);
+          } else {
+            const unsigned o = DIRECTK && pc < 2 ? kdir
+                               : rem >= 1024 || lofs < (unsigned)rem ? lofs : 0u;
+            stg[i] = *(const u4v*)(src[pc] + 1024 * k + o);
+          }
+        }
+      }
+    }
+  };
   auto fetch = [&](int u, bool may_ring) __attribute__((always_inline)) {
     u = __builtin_amdgcn_readfirstlane(u);          // keep the address math scalar
     if (may_ring && u < nres) {
@@ -455,28 +496,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
         stg[i] = *(const u4v*)(src + (i < C::NIR ? 1024 * i + lofs
                                                  : 1024 * (i - C::NIR) + lofs + 16));
     } else {
-      const int t0 = (u - nres) * C::TPU;
-#pragma unroll
-      for (int j = 0; j < C::TPU; ++j) {
-        int t = t0 + j < nqt ? t0 + j : nqt - 1;
-        t = t > 0 ? t : 0;
-        const unsigned po = (unsigned)t * C::PL;
-        const uint8_t* src[6] = {kh_base + po, kl_base + po, vh_base + po, vl_base + po,
-                                 vsz_base + (unsigned)t * C::VSZB,
-                                 ksz_base + (unsigned)(t / tiles_per_group) * C::KSZB};
-        constexpr int bytes[6] = {C::PL, C::TWO ? C::PL : 0, C::PL, C::TWO ? C::PL : 0,
-                                  C::VSZB, C::KSZB};
-        int i = j * C::NI_TILE;
-#pragma unroll
-        for (int pc = 0; pc < 6; ++pc)
-#pragma unroll
-          for (int k = 0; k < chunks_of(bytes[pc]); ++k, ++i) {
-            const int rem = bytes[pc] - 1024 * k;
-            const unsigned o = DIRECTK && pc < 2 ? kdir
-                               : rem >= 1024 || lofs < (unsigned)rem ? lofs : 0u;
-            stg[i] = *(const u4v*)(src[pc] + 1024 * k + o);
-          }
-      }
+      fetch_quant(u, 3);
     }
   };
   auto commit = [&](int u) __attribute__((always_inline)) {
@@ -499,7 +519,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
           for (int k = 0; k < chunks_of(bytes[pc]); ++k, ++i) {
             const int rem = bytes[pc] - 1024 * k;
             const unsigned o = pc < 2 ? 16u * kpat : pc < 4 ? 16u * vpat : lofs;
-            if (!(DIRECTK && pc < 2) && (rem >= 1024 || lofs < (unsigned)rem))
+            if (!(DIRECTK && pc < 4) && (rem >= 1024 || lofs < (unsigned)rem))
               *(u4v*)(stages + j * C::TILE + offs[pc] + 1024 * k + o) = stg[i];
           }
       }
@@ -764,8 +784,8 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
         ak[st][ks] = u4v{r[0], r[1], r[2], r[3]};
       }
     }
-    if constexpr (DIRECTK) {
-      if (u + 1 < u1) fetch(u + 1, false);   // the buffer is free now
+    if constexpr (DIRECTK) {   // key and scale registers are free now
+      fetch_quant(__builtin_amdgcn_readfirstlane(u + 1 < u1 ? u + 1 : u), 1);
     }
     const int grp = t / tiles_per_group;
     if (may_build && grp != cur_grp) {
@@ -799,7 +819,17 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
       }
     }
     unsigned vh[C::NDV], vl[C::TWO ? C::NDV : 1];
-    if constexpr (SWZ) {      // halves of lane l's 32 bytes, swapped when bit 2 of l is set
+    if constexpr (DIRECTK) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        vh[k] = stg[kFirst[2]][k];
+        vh[4 + k] = stg[kFirst[2] + 1][k];
+        if constexpr (C::TWO) {
+          vl[k] = stg[kFirst[3]][k];
+          vl[4 + k] = stg[kFirst[3] + 1][k];
+        }
+      }
+    } else if constexpr (SWZ) {   // halves of lane l's 32 bytes, swapped when bit 2 of l is set
       const int s0 = (lane >> 2) & 1;
       const int v0 = (2 * lane + s0) * 16, v1 = (2 * lane + 1 - s0) * 16;
       lds_read<4>(tb + C::O_VH + v0, vh);
@@ -829,6 +859,9 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
         acc[rt][mt] = mfma16(av, bp[rt][mt / (MT / NG)], acc[rt][mt]);
+    }
+    if constexpr (DIRECTK) {   // value registers are free now
+      fetch_quant(__builtin_amdgcn_readfirstlane(u + 1 < u1 ? u + 1 : u), 2);
     }
   };
 
