@@ -749,7 +749,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   };
 
   // ---- one quantized 32-token tile from LDS
-  auto quant_tile = [&](const unsigned char* tb, int t, bool may_build, int u)
+  auto quant_tile = [&](const unsigned char* tb, int t, bool may_build, int u, bool next)
       __attribute__((always_inline)) {
     u4v ak[2][KS];
 #pragma unroll
@@ -785,7 +785,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
       }
     }
     if constexpr (DIRECTK) {   // key and scale registers are free now
-      fetch_quant(__builtin_amdgcn_readfirstlane(u + 1 < u1 ? u + 1 : u), 1);
+      if (next) fetch_quant(__builtin_amdgcn_readfirstlane(u + 1), 1);
     }
     const int grp = t / tiles_per_group;
     if (may_build && grp != cur_grp) {
@@ -861,7 +861,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
         acc[rt][mt] = mfma16(av, bp[rt][mt / (MT / NG)], acc[rt][mt]);
     }
     if constexpr (DIRECTK) {   // value registers are free now
-      fetch_quant(__builtin_amdgcn_readfirstlane(u + 1 < u1 ? u + 1 : u), 2);
+      if (next) fetch_quant(__builtin_amdgcn_readfirstlane(u + 1), 2);
     }
   };
 
@@ -957,11 +957,14 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   // may_build = false when every tile of the unit is known to belong to
   // the current key group: the inner loop below then carries the B
   // operands unchanged, so they stay in place in registers.
-  auto quant_unit = [&](int u, bool may_build) __attribute__((always_inline)) {
+  // next = false only at the run's last unit (a call site of its own, so
+  // `next` is a constant and the loop keeps one load path): nothing is left
+  // in flight after the loop.
+  auto quant_unit = [&](int u, bool may_build, bool next) __attribute__((always_inline)) {
     const int t0 = (u - nres) * C::TPU;
 #pragma unroll
     for (int j = 0; j < C::TPU; ++j)
-      if (t0 + j < nqt) quant_tile(stages + j * C::TILE, t0 + j, may_build, u);
+      if (t0 + j < nqt) quant_tile(stages + j * C::TILE, t0 + j, may_build, u, next);
   };
   auto in_group = [&](int u) __attribute__((always_inline)) {
     const int t0 = (u - nres) * C::TPU;
@@ -977,14 +980,19 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
       step(u + 1, false);
       ring_v(stages, u >> 1);
     }
-    while (u < u1) {
+    const int ul = u1 - 1;
+    while (u < ul) {
       step(u, true);
-      quant_unit(u, true);
+      quant_unit(u, true, true);
       ++u;
-      for (; u < u1 && in_group(u); ++u) {
+      for (; u < ul && in_group(u); ++u) {
         step(u, true);
-        quant_unit(u, false);
+        quant_unit(u, false, true);
       }
+    }
+    if (u < u1) {                      // the last unit, a quantized one
+      step(u, true);
+      quant_unit(u, true, false);
     }
   }
 
