@@ -388,8 +388,12 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   const int nres = 2 * nrt;                      // ring units
   const int U = nres + (nqt + C::TPU - 1) / C::TPU;
   const int64_t Wt = (int64_t)S * NS;
+  // The runs split the work evenly, counted in half-units: a ring unit (the
+  // K or the V of a fp16 tile) weighs one, a quantized unit two.
+  const int64_t W2 = nres + 2LL * (U - nres);
   auto bound = [&](int64_t x) __attribute__((always_inline)) {
-    int v = (int)(x * U / Wt);
+    const int w = (int)(x * W2 / Wt);
+    int v = w <= nres ? w : nres + (w - nres + 1) / 2;
     if (v < nres && (v & 1)) ++v;                // keep K/V pairs whole
     return v;
   };
