@@ -82,7 +82,6 @@ int hip_fail(hipError_t e, const char* what) {
 // sized for up to kSlotsBound slots (256 CUs x 2 workgroups) and never more
 // splits than the cache has units of work for.
 constexpr int kSlotsBound = 512;
-constexpr int kMaxSplits = 1024;   // (m, l) of each split fit the merge LDS
 
 int rows_pad_of(int T, int Hq, int Hkv) {
   return T * (Hq / Hkv) <= 16 ? 16 : 32;
@@ -95,7 +94,7 @@ int s_alloc_of(const kvq_cache* c) {
   int64_t s = 4 * cdiv(kSlotsBound, nb);
   const int64_t by_units = cdiv(units_max, kWavesPerGroup);
   if (s > by_units) s = by_units;
-  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > kvq::kMaxSplits) s = kvq::kMaxSplits;
   return s < 1 ? 1 : (int)s;
 }
 

@@ -122,6 +122,15 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a full __syncthreads
+// would also drain those).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
 // l^48) with the lane-swap permutes: the operands are combined in the same
 // order on every lane, so all four get bit-identical results.
@@ -272,82 +281,95 @@ struct Cfg {
   static constexpr int NW = NRT == 1 ? 8 : 4;
   static constexpr int NS = NW / NH;             // unit streams per workgroup
   // one LDS stage per wave: a wave writes and reads its own stage, in order;
-  // the stream-merge slabs reuse the stage area after the unit loop
+  // the stream-merge slabs reuse the stage and q area after the unit loop
   static constexpr int DP = D + 4;               // merge slab row (floats)
-  static constexpr int MERGE = (NS / 2) * RTT * 16 * (DP + 2) * 4;   // n - ceil(n/2) <= NS/2
-  static constexpr int SAREA = NW * STAGE > MERGE ? NW * STAGE : MERGE;
-  static constexpr int LDS = SAREA + QB;
+  static constexpr int MERGE = NS * RP * (DP + 2) * 4;   // o rows + (m, l)
+  static constexpr int SAREA = NW * STAGE;
+  static constexpr int LDS = SAREA + QB > MERGE ? SAREA + QB : MERGE;
   static_assert(LDS <= kLdsBytes, "LDS");
 };
 
 // Merge kernel, one workgroup per (block, row): combines the row's S split
-// partials by log-sum-exp.  Every thread first issues the loads of its
-// share of the o rows (up to PRE per thread) and of the (m, l) pairs, so
-// the whole kernel waits on one round trip; the row max and sum are wave
-// reductions through LDS, the o rows are summed by NT/D thread groups.
+// partials by log-sum-exp.  Thread (pg, cq) owns columns 4cq..4cq+3 of the
+// splits pg, pg + NPART, ...  Every thread issues its (m, l) loads and then
+// the 16-byte loads of its first PRE splits before it waits, so a row with
+// up to NPART * PRE splits costs one round trip.  The row max and sum are
+// wave reductions through LDS; the NPART column sums meet in LDS.
 template <int D, int RP>
 __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
-  constexpr int NT = 256;
-  constexpr int NPART = NT / D;          // thread groups over the splits
-  constexpr int PRE = 16;                // o values loaded up front
-  __shared__ float lds[2 * 1024 + 8 + NT];
+  constexpr int NT = 256, DQ = D / 4;
+  constexpr int NPART = NT / DQ;         // thread groups over the splits
+  constexpr int PRE = 8;                 // o quads loaded up front
+  constexpr int MLR = kMaxSplits / NT;   // (m, l) pairs per thread
+  __shared__ float sw[kMaxSplits];       // split weights 2^(m - M)
+  __shared__ float red[8];               // wave max, then wave sums
+  __shared__ f4v part[NPART][DQ];
   const int S = a.S;
   const int64_t blk = blockIdx.x / a.rows;
   const int row = (int)(blockIdx.x % a.rows);
   const int tid = threadIdx.x, wave = tid / kWave;
   const int64_t pstride = (int64_t)RP * (D + 2);
   const float* pblk = a.ws + blk * a.s_alloc * pstride;
-  float* sm = lds;              // [S] m, then weights
-  float* sl = lds + S;          // [S] l
-  float* red = lds + 2 * S;     // [8] wave partials
-  float* part = red + 8;        // [NPART][D]
-  const int c = tid % D, pg = tid / D;
-  const float* src = pblk + row * D + c;
-  float x[PRE];
+  const int cq = tid % DQ, pg = tid / DQ;
+  const float* src = pblk + row * D + 4 * cq;
+  float mr[MLR], lr[MLR];
+#pragma unroll
+  for (int j = 0; j < MLR; ++j) {
+    const int sp = tid + j * NT;
+    mr[j] = sp < S ? pblk[sp * pstride + RP * D + row] : -INFINITY;
+    lr[j] = sp < S ? pblk[sp * pstride + RP * D + RP + row] : 0.f;
+  }
+  f4v x[PRE];
 #pragma unroll
   for (int k = 0; k < PRE; ++k) {
     const int sp = pg + k * NPART;
-    x[k] = sp < S ? src[sp * pstride] : 0.f;
+    x[k] = sp < S ? *(const f4v*)(src + sp * pstride) : f4v{0.f, 0.f, 0.f, 0.f};
   }
-  for (int sp = tid; sp < S; sp += NT) {
-    sm[sp] = pblk[sp * pstride + RP * D + row];
-    sl[sp] = pblk[sp * pstride + RP * D + RP + row];
-  }
-  __syncthreads();
   float M = -INFINITY;
-  for (int sp = tid; sp < S; sp += NT) M = fmaxf(M, sm[sp]);
+#pragma unroll
+  for (int j = 0; j < MLR; ++j) M = fmaxf(M, mr[j]);
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
   if ((tid & (kWave - 1)) == 0) red[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float ls = 0.f;
-  for (int sp = tid; sp < S; sp += NT) {
-    const float e = sm[sp] == -INFINITY ? 0.f : fast_exp2(sm[sp] - M);
-    sm[sp] = e;
-    ls += sl[sp] * e;
+#pragma unroll
+  for (int j = 0; j < MLR; ++j) {
+    const int sp = tid + j * NT;
+    if (sp < S) {
+      const float e = mr[j] == -INFINITY ? 0.f : fast_exp2(mr[j] - M);
+      sw[sp] = e;
+      ls += lr[j] * e;
+    }
   }
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) ls += __shfl_xor(ls, o);
   if ((tid & (kWave - 1)) == 0) red[4 + wave] = ls;
   __syncthreads();
   const float lsum = (red[4] + red[5]) + (red[6] + red[7]);
-  float o = 0.f;
+  f4v o = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < PRE; ++k) {
     const int sp = pg + k * NPART;
-    if (sp < S) o += sm[sp] * x[k];
+    if (sp < S) o += x[k] * sw[sp];
   }
-  for (int sp = pg + PRE * NPART; sp < S; sp += NPART) o += sm[sp] * src[sp * pstride];
-  part[pg * D + c] = o;
+  for (int sp = pg + PRE * NPART; sp < S; sp += NPART)
+    o += *(const f4v*)(src + sp * pstride) * sw[sp];
+  part[pg][cq] = o;
   __syncthreads();
   const int b = (int)(blk / a.g.Hkv), kvh = (int)(blk % a.g.Hkv);
   const int t = row / a.gs, h = kvh * a.gs + row % a.gs;
   if (pg == 0) {
-    float tot = 0.f;
+    f4v tot = part[0][cq];
 #pragma unroll
-    for (int k = 0; k < NPART; ++k) tot += part[k * D + c];
-    a.out[(((int64_t)b * a.T + t) * a.Hq + h) * D + c] = __float2half(tot / lsum);
+    for (int k = 1; k < NPART; ++k) tot += part[k][cq];
+    const __half2 o01 = __halves2half2(__float2half(tot[0] / lsum), __float2half(tot[1] / lsum));
+    const __half2 o23 = __halves2half2(__float2half(tot[2] / lsum), __float2half(tot[3] / lsum));
+    uint2 w;
+    w.x = *(const unsigned*)&o01;
+    w.y = *(const unsigned*)&o23;
+    *(uint2*)(a.out + (((int64_t)b * a.T + t) * a.Hq + h) * D + 4 * cq) = w;
   }
   if (tid == 0 && a.lse)
     a.lse[((int64_t)b * a.Hq + h) * a.T + t] = (M + __log2f(lsum)) * kLn2;
@@ -356,8 +378,8 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
 // Dynamic LDS of the split kernel:
 //   stages  [NW][STAGE]       each wave's unit stage
 //   s_q     fp16 [RP][D]      this block's query rows (zero past `rows`)
-// After the unit loop the stage area holds the stream-merge slabs
-//   slab float [NS/2][RTT][16][D+4], ml float [NS/2][RTT][2][16].
+// After the unit loop the same bytes hold the stream-merge slabs
+//   slab float [NS][RP][D+4], ml float [NS][2][RP].
 template <int PATH, int D, int NG, int NRT, bool PAIR>
 __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     attn_kernel(const AttnArgs a) {
@@ -553,9 +575,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
       const int k = tid + i * NT;
       if (k < RP * (D / 8)) *(u4v*)(s_q + 8 * k) = qv[i];
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    lds_barrier();
   }
 
   // ---- per-wave state (NRT 16-row tiles)
@@ -1012,74 +1032,50 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
       acc[rt][mt] = acc[rt][mt] * kOScale + zacc[rt][mt / (MT / NG)];
   }
 
-  // ---- merge the NS streams (per row tile) through LDS, halving each step
-  // slab rows padded by 4 floats: the 16 rows of a put/take land in
-  // different banks
+  // ---- merge the NS streams through LDS in one step: every stream writes
+  // its (o, m, l) rows, then each thread of the workgroup combines the NS
+  // states of one (row, 4 columns) item and writes it to the workgroup
+  // partial o[RP][D], m[RP], l[RP]. Slab rows are padded by 4 floats, so
+  // the 16 rows of a wave's write land in different banks. Rows past `rows`
+  // are never read by the merge and are not written.
   constexpr int DP = C::DP;
-  float* s_slab = (float*)smem;
-  float* s_ml = s_slab + (NS / 2) * RTT * 16 * DP;
-  auto put = [&](int slot_m) __attribute__((always_inline)) {
+  constexpr int SLAB = RP * DP;
+  float* s_slab = (float*)smem;                  // [NS][RP][DP]
+  float* s_ml = s_slab + NS * SLAB;              // [NS][m, l][RP]
+  lds_barrier();                                 // every stage and q read done
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int tt = slot_m * RTT + h * NRT + rt;
-      float* o = s_slab + tt * 16 * DP;
-      float* ml = s_ml + tt * 32;
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int row = row_of(rt);
+    float* o = s_slab + strm * SLAB + row * DP;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        *(f4v*)(o + l16 * DP + 16 * mt + 4 * gq) = acc[rt][mt];
-      if (gq == 0) {
-        ml[l16] = m_ref[rt];
-        ml[16 + l16] = l_run[rt];
-      }
+    for (int mt = 0; mt < MT; ++mt) *(f4v*)(o + 16 * mt + 4 * gq) = acc[rt][mt];
+    if (gq == 0) {
+      s_ml[strm * 2 * RP + row] = m_ref[rt];
+      s_ml[strm * 2 * RP + RP + row] = l_run[rt];
     }
-  };
-  auto take = [&](int slot_m) __attribute__((always_inline)) {
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int tt = slot_m * RTT + h * NRT + rt;
-      const float* o = s_slab + tt * 16 * DP;
-      const float* ml = s_ml + tt * 32;
-      const float mo = ml[l16], lo = ml[16 + l16];
-      const float M = fmaxf(m_ref[rt], mo);
-      const float fa = M == -INFINITY ? 0.f : fast_exp2(m_ref[rt] - M);
-      const float fb = M == -INFINITY ? 0.f : fast_exp2(mo - M);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[rt][mt] = acc[rt][mt] * fa +
-                      *(const f4v*)(o + l16 * DP + 16 * mt + 4 * gq) * fb;
-      l_run[rt] = l_run[rt] * fa + lo * fb;
-      m_ref[rt] = M;
-    }
-  };
-  __syncthreads();   // every stream is done with its stages
-  // halving steps over n live streams: streams [h, n) hand their state to
-  // streams [0, n - h), h = ceil(n / 2)
-#pragma unroll
-  for (int n = NS; n > 1; n = (n + 1) / 2) {
-    const int hh = (n + 1) / 2;
-    if (strm >= hh && strm < n) put(strm - hh);
-    __syncthreads();
-    if (strm < n - hh) take(strm);
-    __syncthreads();
   }
-
-  // ---- workgroup partial: o[RP][D], m[RP], l[RP] (rows past `rows` are
-  // never read by the merge and are not written)
-  if (strm == 0) {
-    const int64_t pstride = (int64_t)RP * (D + 2);
-    float* po = a.ws + (blk * a.s_alloc + split) * pstride;
+  lds_barrier();
+  const int64_t pstride = (int64_t)RP * (D + 2);
+  float* po = a.ws + (blk * a.s_alloc + split) * pstride;
+  constexpr int DQ = D / 4;
+  for (int it = tid; it < a.rows * DQ; it += NT) {
+    const int row = it / DQ, c = 4 * (it % DQ);
+    float M = -INFINITY;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int row = row_of(rt);
-      if (16 * (h * NRT + rt) < a.rows) {
+    for (int st = 0; st < NS; ++st) M = fmaxf(M, s_ml[st * 2 * RP + row]);
+    f4v o = f4v{0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          *(f4v*)(po + row * D + 16 * mt + 4 * gq) = acc[rt][mt];
-        if (gq == 0) {
-          po[RP * D + row] = m_ref[rt];
-          po[RP * D + RP + row] = l_run[rt];
-        }
-      }
+    for (int st = 0; st < NS; ++st) {
+      const float ms = s_ml[st * 2 * RP + row];
+      const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+      o += *(const f4v*)(s_slab + st * SLAB + row * DP + c) * w;
+      l += s_ml[st * 2 * RP + RP + row] * w;
+    }
+    *(f4v*)(po + row * D + c) = o;
+    if (c == 0) {
+      po[RP * D + row] = M;
+      po[RP * D + RP + row] = l;
     }
   }
 }

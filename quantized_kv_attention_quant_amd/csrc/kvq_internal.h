@@ -12,6 +12,7 @@ namespace kvq {
 
 constexpr int kTile = 32;       // tokens per V tile / ring tile
 constexpr int kWave = 64;       // CDNA wavefront width
+constexpr int kMaxSplits = 1024;   // split partials per block; their weights fit the merge LDS
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) {
   return (a + b - 1) / b;
