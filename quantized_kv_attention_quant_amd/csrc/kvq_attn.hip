@@ -305,8 +305,8 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
   __shared__ float red[8];               // wave max, then wave sums
   __shared__ f4v part[NPART][DQ];
   const int S = a.S;
-  const int64_t blk = blockIdx.x / a.rows;
-  const int row = (int)(blockIdx.x % a.rows);
+  const int row = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int64_t blk = (int64_t)b * a.g.Hkv + kvh;
   const int tid = threadIdx.x, wave = tid / kWave;
   const int64_t pstride = (int64_t)RP * (D + 2);
   const float* pblk = a.ws + blk * a.s_alloc * pstride;
@@ -358,7 +358,6 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
     o += *(const f4v*)(src + sp * pstride) * sw[sp];
   part[pg][cq] = o;
   __syncthreads();
-  const int b = (int)(blk / a.g.Hkv), kvh = (int)(blk % a.g.Hkv);
   const int t = row / a.gs, h = kvh * a.gs + row % a.gs;
   if (pg == 0) {
     f4v tot = part[0][cq];
@@ -391,9 +390,8 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
 
   const CacheGeom& g = a.g;
   const int S = a.S;
-  const int64_t blk = blockIdx.x / S;
-  const int split = (int)(blockIdx.x % S);
-  const int b = (int)(blk / g.Hkv), kvh = (int)(blk % g.Hkv);
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int64_t blk = (int64_t)b * g.Hkv + kvh;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int strm = PAIR ? wave >> 1 : wave;      // stream in the workgroup
@@ -409,17 +407,20 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   const int nqt = (int)(a.n_q / kTile), nrt = (int)cdiv(a.n_r, kTile);
   const int nres = 2 * nrt;                      // ring units
   const int U = nres + (nqt + C::TPU - 1) / C::TPU;
-  const int64_t Wt = (int64_t)S * NS;
+  const int Wt = S * NS;
   // The runs split the work evenly, counted in half-units: a ring unit (the
-  // K or the V of a fp16 tile) weighs one, a quantized unit two.
-  const int64_t W2 = nres + 2LL * (U - nres);
-  auto bound = [&](int64_t x) __attribute__((always_inline)) {
-    const int w = (int)(x * W2 / Wt);
+  // K or the V of a fp16 tile) weighs one, a quantized unit two.  The
+  // quotient floor(x W2 / Wt) is taken in fp64, which is exact here (x W2 <
+  // 2^40, and a non-integral quotient is at least 1/Wt from an integer) and
+  // far cheaper than a 64-bit integer division, which has no instruction.
+  const int W2 = nres + 2 * (U - nres);
+  auto bound = [&](int x) __attribute__((always_inline)) {
+    const int w = (int)((double)x * (double)W2 / (double)Wt);
     int v = w <= nres ? w : nres + (w - nres + 1) / 2;
     if (v < nres && (v & 1)) ++v;                // keep K/V pairs whole
     return v;
   };
-  const int64_t c0s = (int64_t)split * NS;
+  const int c0s = split * NS;
   // wave-uniform: keep them (and everything derived) in scalar registers
   const int u0 = __builtin_amdgcn_readfirstlane(bound(c0s + strm));
   const int u1 = __builtin_amdgcn_readfirstlane(bound(c0s + strm + 1));
@@ -435,8 +436,12 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   const uint8_t* ksz_base = (const uint8_t*)(a.p.k_sz + blk * g.ksz_block);
   const uint8_t* kres_base = (const uint8_t*)(a.p.k_res + blk * g.res_block);
   const uint8_t* vres_base = (const uint8_t*)(a.p.v_res + blk * g.res_block);
-  const int nq_mod = (int)(a.n_q % g.ring);
+  const int nq_mod = a.nq_mod;
   const int tiles_per_group = g.G / kTile;
+  // key group of quantized tile t
+  auto group_of = [&](int t) __attribute__((always_inline)) {
+    return a.grp_shift >= 0 ? t >> a.grp_shift : t / tiles_per_group;
+  };
 
   // ---- staged loads of a unit: fetch loads the unit's chunks into stg
   // (16 bytes per lane, one coalesced instruction per 1 KB chunk), commit
@@ -490,7 +495,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
       const unsigned po = (unsigned)t * C::PL;
       const uint8_t* src[6] = {kh_base + po, kl_base + po, vh_base + po, vl_base + po,
                                vsz_base + (unsigned)t * C::VSZB,
-                               ksz_base + (unsigned)(t / tiles_per_group) * C::KSZB};
+                               ksz_base + (unsigned)group_of(t) * C::KSZB};
       constexpr int order[6] = {0, 1, 4, 5, 2, 3};   // keys and scales first
 #pragma unroll
       for (int oi = 0; oi < 6; ++oi) {
@@ -811,7 +816,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     if constexpr (DIRECTK) {   // key and scale registers are free now
       if (next) fetch_quant(__builtin_amdgcn_readfirstlane(u + 1), 1);
     }
-    const int grp = t / tiles_per_group;
+    const int grp = group_of(t);
     if (may_build && grp != cur_grp) {
       build_quant(tb + C::O_KSZ);
       cur_grp = grp;
@@ -993,7 +998,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   auto in_group = [&](int u) __attribute__((always_inline)) {
     const int t0 = (u - nres) * C::TPU;
     const int t1 = (t0 + C::TPU < nqt ? t0 + C::TPU : nqt) - 1;
-    return t0 / tiles_per_group == cur_grp && t1 / tiles_per_group == cur_grp;
+    return group_of(t0) == cur_grp && group_of(t1) == cur_grp;
   };
   {
     int u = u0;
@@ -1115,11 +1120,20 @@ hipError_t go(AttnArgs a, hipStream_t s) {
   const int64_t nb = (int64_t)a.g.B * a.g.Hkv;
   const int64_t units = 2 * cdiv(a.n_r, kTile) + cdiv(a.n_q / kTile, C::TPU);
   a.S = plan_splits(nb, (int64_t)cus * occ, units, C::NS, a.s_alloc);
+  a.nq_mod = (int)(a.n_q % a.g.ring);
+  const int tpg = a.g.G / kTile;
+  a.grp_shift = -1;
+  for (int k = 0; k < 31; ++k)
+    if (tpg == 1 << k) a.grp_shift = k;
+  // grid: splits x kv heads x batch; consecutive workgroups are consecutive
+  // splits of one block
   hipLaunchKernelGGL((attn_kernel<PATH, D, NG, NRT, PAIR>),
-                     dim3((unsigned)(nb * a.S)), dim3(C::NW * kWave), C::LDS, s, a);
+                     dim3((unsigned)a.S, (unsigned)a.g.Hkv, (unsigned)a.g.B),
+                     dim3(C::NW * kWave), C::LDS, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<D, C::RP>), dim3((unsigned)(nb * a.rows)),
+  hipLaunchKernelGGL((merge_kernel<D, C::RP>),
+                     dim3((unsigned)a.rows, (unsigned)a.g.Hkv, (unsigned)a.g.B),
                      dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -111,6 +111,8 @@ struct AttnArgs {
   int S;            // split workgroups per block (set by the launcher)
   int s_alloc;      // partial slots per block in the workspace
   int rows_pad;     // 16 * row tiles
+  int nq_mod;       // n_q mod ring: ring slot of the first residual token
+  int grp_shift;    // log2(G / 32) when G / 32 is a power of two, else -1
 };
 // Splits per block for nb blocks on `slots` resident workgroup slots, with
 // `units` units of work per block, nw waves per workgroup, at most cap.
