@@ -19,12 +19,14 @@
  *         alongside the output token scores that copy and its top-k KV pairs
  *         are the ones to prefetch.
  *   [MS]  "MSpecKV" (project page).  Abstract: KV-cache traffic dominates
- *         long-context decoding; offloaded KV is stored quantized.
+ *         long-context decoding; offloaded KV is stored quantized and only
+ *         the subsets that are needed are reconstructed on demand.
  *
  * Three entry points do the work: kv_quant_append (quantize-on-append),
  * kv_attn_verify (split-K attention over the quantized prefix plus the
  * fp16 residual buffer, merged by log-sum-exp) and kv_topk (per-kv-head
- * top-k over low-bit scores).  The rest is host-side bookkeeping.
+ * top-k over low-bit scores).  kv_dequant_gather rebuilds fp16 rows of a
+ * requested token subset.  The rest is host-side bookkeeping.
  *
  * Conventions for every call
  *   - Ownership: the caller owns every buffer (host struct and device
@@ -208,6 +210,23 @@ size_t kv_topk_workspace_bytes(const kvq_cache* c, int Hq, int k);
  * use, reusable.  Requires 1 <= k <= 256, Hq % Hkv == 0, Hq/Hkv <= 8. */
 int kv_topk(const kvq_cache* c, const void* q_spec, int Hq, int path, int k,
             int32_t* idx, float* key, void* ws, size_t ws_bytes, void* stream);
+
+/* On-demand reconstruction of a token subset ([MS] Abstract: KV kept in
+ * quantized form, only the subsets that are needed rebuilt on demand).  For
+ * every block (b, kvh) and request i < n, with p = idx[b][kvh][i]:
+ *   0 <= p < n_q (quantized):  k_out/v_out[b][kvh][i][c] =
+ *       fp16_rne( f32(z + f32(code*s)) )   (one IEEE binary32 multiply, one
+ *       add, no fusing), with the token's key-group / value-group (s, z) and
+ *       code = q (KVQ_TARGET, every stored bit) or 16*hi + 7.5 (KVQ_DRAFT4,
+ *       bits == 8 only: the INT4 draft view);
+ *   n_q <= p < n_q + n_r (residual):  the fp16 values in the ring;
+ *   any other p:  fp16 NaN in every channel (nothing outside the cache is
+ *       read).
+ * idx: device int32 [B][Hkv][n]; k_out, v_out: device fp16 [B][Hkv][n][d]
+ * (token-major rows, written in full).  n = 0 enqueues nothing.  No
+ * workspace.  Requires 0 <= n <= 2^24. */
+int kv_dequant_gather(const kvq_cache* c, const int32_t* idx, int n, int path,
+                      void* k_out, void* v_out, void* stream);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* kv_last_error(void);

@@ -15,6 +15,7 @@ Modules
   cache      append / flush / rollback replay of the hierarchical cache
   attention  float64 softmax attention over the dequantized cache
   topk       canonical float32 speculative-token keys and exact top-k
+  gather     on-demand reconstruction of a token subset (binary32-exact)
 
 Sources (cited by page title and section):
   "QuantSpec: Self-Speculative Decoding with Hierarchical Quantized KV Cache"
@@ -25,7 +26,8 @@ Sources (cited by page title and section):
   "SpeCache: Speculative Key-Value Caching for Efficient Generation of LLMs"
       Approach (1/2-bit KIVI copy on the GPU; speculative token's scores
       choose the top-k KV pairs).
-  "MSpecKV" Abstract (KV traffic dominates; offloaded KV stored quantized).
+  "MSpecKV" Abstract (KV traffic dominates; offloaded KV stored quantized,
+      only the needed subsets reconstructed on demand).
 
 Parity status (which function is pinned by what) is listed in each module's
 docstring.  Nothing here is unpinned.

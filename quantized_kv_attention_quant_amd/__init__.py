@@ -2,7 +2,8 @@
 
 Thin ctypes layer over the C ABI declared in ``include/kvq.h``.  The entry
 points keep the C names (``kv_cache_layout``, ``kv_quant_append``,
-``kv_rollback``, ``kv_attn_verify``, ``kv_topk`` and the workspace sizers);
+``kv_rollback``, ``kv_attn_verify``, ``kv_topk``, ``kv_dequant_gather`` and
+the workspace sizers);
 this module only checks tensor shapes/dtypes, passes device pointers and the
 current HIP stream, and turns non-zero return codes into ``KvqError``.  All
 computation happens in the HIP kernels of ``libkvq.so``; PyTorch is used for
@@ -22,7 +23,7 @@ __all__ = [
     "KVQ_TARGET", "KVQ_DRAFT4", "KvqError", "KvqCacheStruct", "lib",
     "kv_cache_layout", "kv_quant_append", "kv_rollback",
     "kv_attn_workspace_bytes", "kv_attn_verify", "kv_topk_workspace_bytes",
-    "kv_topk", "kv_last_error", "QuantKVCache", "LIB_PATH",
+    "kv_topk", "kv_dequant_gather", "kv_last_error", "QuantKVCache", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -87,10 +88,11 @@ def lib() -> ctypes.CDLL:
     L.kv_topk_workspace_bytes.argtypes = [P, i32, i32]
     L.kv_topk_workspace_bytes.restype = sz
     L.kv_topk.argtypes = [P, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    L.kv_dequant_gather.argtypes = [P, vp, i32, i32, vp, vp, vp]
     L.kv_last_error.argtypes = []
     L.kv_last_error.restype = ctypes.c_char_p
     for name in ("kv_cache_layout", "kv_quant_append", "kv_rollback",
-                 "kv_attn_verify", "kv_topk"):
+                 "kv_attn_verify", "kv_topk", "kv_dequant_gather"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -152,6 +154,13 @@ def kv_topk(c: KvqCacheStruct, q_spec, Hq: int, path, k: int, idx, key, ws,
     _check(lib().kv_topk(
         ctypes.byref(c), _ptr(q_spec), Hq, _path(path), k, _ptr(idx),
         _ptr(key), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def kv_dequant_gather(c: KvqCacheStruct, idx, n: int, path, k_out, v_out,
+                      stream=None) -> None:
+    _check(lib().kv_dequant_gather(
+        ctypes.byref(c), _ptr(idx), n, _path(path), _ptr(k_out), _ptr(v_out),
+        _stream(stream)))
 
 
 # ---- torch-owned cache -----------------------------------------------------
@@ -297,3 +306,26 @@ class QuantKVCache:
             ws = self.topk_workspace(Hq, k)
         kv_topk(self.c, q_spec, Hq, path, k, idx, key, ws, stream)
         return idx, key
+
+    def gather(self, idx, path="target", k_out=None, v_out=None, stream=None):
+        """kv_dequant_gather for int32 positions idx [B][Hkv][n]; returns the
+        fp16 rows (k_out, v_out), each [B][Hkv][n][d]."""
+        import torch
+        s = self.shape
+        if (idx.dtype != torch.int32 or not idx.is_cuda
+                or not idx.is_contiguous() or idx.dim() != 3
+                or idx.shape[0] != s.B or idx.shape[1] != s.Hkv):
+            raise ValueError("idx must be contiguous int32 CUDA [B][Hkv][n]")
+        n = idx.shape[2]
+        shape = (s.B, s.Hkv, n, s.d)
+        for t, name in ((k_out, "k_out"), (v_out, "v_out")):
+            if t is not None and (t.dtype != torch.float16 or not t.is_cuda
+                                  or not t.is_contiguous()
+                                  or tuple(t.shape) != shape):
+                raise ValueError(f"{name} must be contiguous fp16 CUDA {shape}")
+        if k_out is None:
+            k_out = torch.empty(shape, dtype=torch.float16, device=idx.device)
+        if v_out is None:
+            v_out = torch.empty(shape, dtype=torch.float16, device=idx.device)
+        kv_dequant_gather(self.c, idx, n, path, k_out, v_out, stream)
+        return k_out, v_out

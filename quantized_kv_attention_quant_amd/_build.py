@@ -17,10 +17,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_attn.hip", "kvq_topk.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_attn.hip", "kvq_topk.hip",
+           "kvq_gather.hip"]
 # Sources whose results must match a binary32 definition bit for bit: no
 # multiply-add fusion anywhere in the translation unit (headers included).
-EXACT = {"kvq_quant.hip", "kvq_topk.hip"}
+EXACT = {"kvq_quant.hip", "kvq_topk.hip", "kvq_gather.hip"}
 # Sources with no NaN inputs by construction: min/max need no canonicalizing
 # of their operands.
 NO_NANS = {"kvq_attn.hip"}

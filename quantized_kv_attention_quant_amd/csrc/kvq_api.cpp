@@ -273,4 +273,32 @@ KVQ_API int kv_topk(const kvq_cache* c, const void* q_spec, int Hq, int path,
   return KVQ_OK;
 }
 
+KVQ_API int kv_dequant_gather(const kvq_cache* c, const int32_t* idx, int n,
+                              int path, void* k_out, void* v_out, void* stream) {
+  int rc = check_cache(c);
+  if (rc) return rc;
+  if (n < 0) return fail(KVQ_EINVAL, "n must be >= 0");
+  if (n > 0 && (!idx || !k_out || !v_out))
+    return fail(KVQ_EINVAL, "idx/k_out/v_out is NULL");
+  if (path != KVQ_TARGET && path != KVQ_DRAFT4)
+    return fail(KVQ_EINVAL, "unknown path %d", path);
+  if (path == KVQ_DRAFT4 && c->bits != 8)
+    return fail(KVQ_EINVAL, "the draft path reads 8-bit caches only");
+  if (n > (1 << 24)) return fail(KVQ_EINVAL, "n must be at most 2^24");
+
+  kvq::GatherArgs a;
+  a.g = kvq::geom_of(c);
+  a.p = kvq::ptrs_of(c);
+  a.idx = idx;
+  a.k_out = (__half*)k_out;
+  a.v_out = (__half*)v_out;
+  a.n_q = c->n_q;
+  a.n_r = c->n_r;
+  a.n = n;
+  a.path = path;
+  hipError_t e = kvq::launch_gather(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_dequant_gather launch");
+  return KVQ_OK;
+}
+
 KVQ_API const char* kv_last_error(void) { return g_err.c_str(); }

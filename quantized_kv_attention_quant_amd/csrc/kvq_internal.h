@@ -119,6 +119,19 @@ struct AttnArgs {
 int plan_splits(int64_t nb, int64_t slots, int64_t units, int nw, int cap);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
+// On-demand reconstruction: see kv_dequant_gather.
+struct GatherArgs {
+  CacheGeom g;
+  CachePtrs p;
+  const int32_t* idx;   // [B][Hkv][n] token positions
+  __half* k_out;        // [B][Hkv][n][d]
+  __half* v_out;        // [B][Hkv][n][d]
+  int64_t n_q, n_r;
+  int n;
+  int path;             // KVQ_TARGET / KVQ_DRAFT4
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+
 struct TopkArgs {
   CacheGeom g;
   CachePtrs p;

@@ -28,7 +28,8 @@ def test_exports_match_header():
     names = _declared()
     assert names == {"kv_cache_layout", "kv_quant_append", "kv_rollback",
                      "kv_attn_workspace_bytes", "kv_attn_verify",
-                     "kv_topk_workspace_bytes", "kv_topk", "kv_last_error"}
+                     "kv_topk_workspace_bytes", "kv_topk", "kv_dequant_gather",
+                     "kv_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", kq.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -178,6 +179,21 @@ def test_topk_errors_before_launch():
     assert _code(lambda: call(ws=FakeT(8))) == kq.KVQ_EWORKSPACE
     low = _fake_cache(bits=1, G=32, Gv=32, R=32, n_q=1024, n_r=8)
     assert _code(lambda: call(c=low, path=kq.KVQ_DRAFT4)) == kq.KVQ_EINVAL
+
+
+def test_gather_errors_before_launch():
+    c = _fake_cache(n_q=1024, n_r=40)
+    call = lambda n=5, path=0, c=c, idx=FakeT(), ko=FakeT(), vo=FakeT(): \
+        kq.kv_dequant_gather(c, idx, n, path, ko, vo, 0)
+    assert _code(lambda: call(n=-1)) == kq.KVQ_EINVAL
+    assert _code(lambda: call(path=7)) == kq.KVQ_EINVAL
+    assert _code(lambda: call(idx=None)) == kq.KVQ_EINVAL
+    assert _code(lambda: call(vo=None)) == kq.KVQ_EINVAL
+    assert _code(lambda: call(n=(1 << 24) + 1)) == kq.KVQ_EINVAL
+    low = _fake_cache(bits=2, G=32, Gv=32, R=32, n_q=1024, n_r=8)
+    assert _code(lambda: call(c=low, path=kq.KVQ_DRAFT4)) == kq.KVQ_EINVAL
+    # n = 0 enqueues nothing, so it succeeds without touching the device
+    kq.kv_dequant_gather(c, None, 0, 0, None, None, 0)
 
 
 def test_uninitialised_cache_rejected():
