@@ -18,7 +18,10 @@ so that, as in a model with many layers, a step never finds its cache in the
 
 The JSON line reports us/step (wall clock over the timed steps), the
 dominant kernel's duration (HIP events on its stream) against the HBM
-roofline, and the CPU oracle timed on the host on one full step.
+roofline, and the CPU oracle timed on the host on one full step.  Beside the
+step ("comparators", not part of the step's value): the same attention with
+the whole context in the fp16 residual buffer (the FP16 comparator), and
+kv_dequant_gather of 64 positions per kv head.
 """
 from __future__ import annotations
 
@@ -133,6 +136,89 @@ def calibrate_copy(nbytes=256 << 20, reps=3):
     torch.cuda.synchronize()
 
 
+def comparators(w, seed, K, V, caches, q_draft, q_verify, k_new, v_new,
+                steps=50):
+    """Two side measurements on the same workload (not part of the step):
+      fp16 comparator: the same attention with the whole 32K context in the
+        fp16 residual buffer (no quantized prefix), T=7 and T=1, against the
+        INT8 / INT4 paths over the quantized cache;
+      on-demand reconstruction: kv_dequant_gather of 64 positions per kv
+        head (a top-k fetch), target path, on the quantized cache copies.
+    Both use HIP events on the launch stream; each call reads a different
+    cache copy, as in the step."""
+    import torch
+    import quantized_kv_attention_quant_amd as kq
+    dev = q_draft.device
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    L0 = w.L - T_VERIFY
+    shape = kq.Shape(B=w.B, Hkv=w.Hkv, d=w.d, G=w.G, Gv=w.Gv, bits=w.bits,
+                     R=w.L, L_max=w.G, max_append=32)
+    base = kq.QuantKVCache(shape, device=dev)
+    base.append(torch.from_numpy(np.ascontiguousarray(K[:, :L0])).to(dev),
+                torch.from_numpy(np.ascontiguousarray(V[:, :L0])).to(dev))
+    n_fp16 = 4                                   # 4 x 134 MB > Infinity Cache
+    fcs = [base] + [base.clone() for _ in range(n_fp16 - 1)]
+    assert base.n_q == 0 and base.n_r == L0
+    sm = w.d ** -0.5
+    ws = fcs[0].attn_workspace(T_VERIFY, w.Hq)
+    out_v, out_d = torch.empty_like(q_verify), torch.empty_like(q_draft)
+
+    def timed(fn, n):
+        ts = []
+        for i in range(n + 5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(i)
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ts[5:]]) * 1e3
+
+    # time only the attention: record around the verify call
+    def fp16_attn(T, q, out):
+        ts = []
+        for i in range(steps + 5):
+            c = fcs[i % n_fp16]
+            kq.kv_quant_append(c.c, k_new, v_new, T_VERIFY, sh)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            kq.kv_attn_verify(c.c, q, T, w.Hq, kq.KVQ_TARGET, sm, out, None, ws, sh)
+            e1.record(stream)
+            kq.kv_rollback(c.c, T_VERIFY)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ts[5:]]) * 1e3
+
+    f7 = fp16_attn(T_VERIFY, q_verify, out_v)
+    f1 = fp16_attn(T_DRAFT, q_draft, out_d)
+    bytes_f7 = algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv, 0, w.L, T_VERIFY, 8)
+    bytes_f1 = algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv, 0, w.L, T_DRAFT, 8)
+    del fcs, base
+    torch.cuda.empty_cache()
+
+    rng = np.random.default_rng(seed + 7)
+    n_g = 64
+    idx = torch.from_numpy(rng.integers(0, w.L, (w.B, w.Hkv, n_g)).astype(np.int32)).to(dev)
+    k_out = torch.empty((w.B, w.Hkv, n_g, w.d), dtype=torch.float16, device=dev)
+    v_out = torch.empty_like(k_out)
+    for c in caches:
+        kq.kv_quant_append(c.c, k_new, v_new, T_VERIFY, sh)
+    g = timed(lambda i: kq.kv_dequant_gather(caches[i % N_COPIES].c, idx, n_g,
+                                             kq.KVQ_TARGET, k_out, v_out, sh),
+              steps)
+    for c in caches:
+        kq.kv_rollback(c.c, T_VERIFY)
+    torch.cuda.synchronize()
+    return {
+        "fp16_verify_t7_us": round(float(np.median(f7)), 3),
+        "fp16_decode_t1_us": round(float(np.median(f1)), 3),
+        "fp16_verify_t7_gbps": round(bytes_f7 / (f7.mean() * 1e-6) / 1e9, 1),
+        "fp16_decode_t1_gbps": round(bytes_f1 / (f1.mean() * 1e-6) / 1e9, 1),
+        "gather_64_per_head_us": round(float(np.median(g)), 3),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +226,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-comparators", action="store_true",
+                    help="skip the fp16-comparator and gather measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (profiling scale)")
     args = ap.parse_args()
@@ -265,6 +353,15 @@ def main():
             "bytes_per_launch": bytes_verify,
         },
     }
+    if not args.no_comparators:
+        comp = comparators(w, args.seed, K, V, caches, q_draft, q_verify,
+                           k_new, v_new)
+        ku = res["kernels_us"]
+        comp["int8_vs_fp16_speedup"] = round(comp["fp16_verify_t7_us"]
+                                             / ku["verify_int8_t7"], 3)
+        comp["int4_vs_fp16_speedup"] = round(comp["fp16_decode_t1_us"]
+                                             / ku["draft_int4_t1"], 3)
+        res["comparators"] = comp
     if args.calibrate_copy:
         calibrate_copy()
     if not args.no_cpu_baseline:

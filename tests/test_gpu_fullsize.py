@@ -8,6 +8,8 @@ The outputs of the sampled blocks (attention rows, LSE, top-k indices and
 keys) are compared with the oracle run on those blocks alone, following the
 same sequence of appends and rollbacks.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -119,6 +121,26 @@ def test_llama3_32k_bench_step():
     torch.cuda.synchronize()
     assert np.array_equal(d0, d1.cpu().numpy())
     assert np.array_equal(t0, t1.cpu().numpy())
+
+
+def test_llama3_32k_fp16_comparator():
+    """The FP16 comparator: the 32K context held entirely in the fp16
+    residual buffer (R = L, no quantized prefix), verify T=7 and decode T=1,
+    against the oracle's plain softmax attention on sampled blocks."""
+    w = dataclasses.replace(synth.WORKLOADS["llama3_8b_32k"],
+                            R=synth.WORKLOADS["llama3_8b_32k"].L)
+    say("[gpu] full size llama3_8b_32k, all-fp16 context: T=7 and T=1")
+    sampled = [(0, 1), (0, 6)]
+    K, V, host = device_tokens(w, 0, w.L, sampled)
+    cache = kq.QuantKVCache(shape_for(w, L_max=w.G, max_append=32))
+    mirror = Mirror(w, host)
+    cache.append(K[:, :w.L - 7].contiguous(), V[:, :w.L - 7].contiguous())
+    mirror.append(0, w.L - 7)
+    cache.append(K[:, w.L - 7:].contiguous(), V[:, w.L - 7:].contiguous())
+    mirror.append(w.L - 7, w.L)
+    assert (cache.n_q, cache.n_r) == (0, w.L)
+    check_attention(cache, mirror, synth.queries(w, 3, 7), "target", "fp16 T=7")
+    check_attention(cache, mirror, synth.queries(w, 4, 1), "target", "fp16 T=1")
 
 
 def test_lwm_128k_append6_rollback2():
