@@ -21,7 +21,11 @@ scaled_dot_product_attention (float64, CPU) when the whole context is in the
 residual buffer, equality with the same routine applied to the dequantized
 cache, row t of a verify equal to a T=1 decode over the first pos(t)+1
 tokens, GQA equal to MHA with repeated kv heads, and the draft ignoring the
-low nibble plane.
+low nibble plane.  Exact substitution (``attend_exact``): no positions gives
+``attend``; substituting every quantized token by its original fp16 value
+gives SDPA over the original tokens for that row and leaves the other rows
+as they were; substituting a token by its own dequantized value (when that
+value is an fp16 number) changes nothing.
 """
 from __future__ import annotations
 
@@ -29,7 +33,7 @@ import numpy as np
 
 from . import quant
 
-__all__ = ["block_kv", "attend_block", "attend"]
+__all__ = ["block_kv", "attend_block", "attend", "attend_exact"]
 
 
 def block_kv(kq, ks, kz, vq, vs, vz, rk, rv, G, Gv, path):
@@ -83,4 +87,35 @@ def attend(rep, q16: np.ndarray, path: str, sm_scale: float):
             o, s = attend_block(q16[b, :, h * gs:(h + 1) * gs], K, V, sm_scale)
             out[b, :, h * gs:(h + 1) * gs] = o
             lse[b, h * gs:(h + 1) * gs] = s
+    return out, lse
+
+
+def attend_exact(rep, q16: np.ndarray, path: str, sm_scale: float,
+                 idx: np.ndarray, k_exact: np.ndarray, v_exact: np.ndarray,
+                 t_exact: int = 0):
+    """``attend`` with exact substitution for one query row (SpeCache page,
+    Approach: the KV pairs the speculative token ranks highest are fetched
+    in full precision and used for the output token).  Query row t_exact
+    reads the fp16 values k_exact/v_exact at the quantized positions
+    idx[b, kvh] (entries < 0 are skipped) instead of their dequantized
+    values; every other row reads the cache as ``attend`` does.
+    idx: (B, Hkv, n) int, distinct positions < n_q per block;
+    k_exact, v_exact: (B, Hkv, n, d) fp16.  Returns out, lse as ``attend``."""
+    out, lse = attend(rep, q16, path, sm_scale)
+    B, T, Hq, d = q16.shape
+    gs = Hq // rep.Hkv
+    for b in range(B):
+        for h in range(rep.Hkv):
+            K, V = block_kv(rep.kq[b, h], rep.ks[b, h], rep.kz[b, h],
+                            rep.vq[b, h], rep.vs[b, h], rep.vz[b, h],
+                            rep.rk[b, h], rep.rv[b, h], rep.G, rep.Gv, path)
+            sel = np.asarray(idx[b, h])
+            keep = sel >= 0
+            assert (sel[keep] < rep.n_q).all()
+            assert len(np.unique(sel[keep])) == keep.sum()
+            K[sel[keep]] = k_exact[b, h][keep].astype(np.float64)
+            V[sel[keep]] = v_exact[b, h][keep].astype(np.float64)
+            o, s = attend_block(q16[b, :, h * gs:(h + 1) * gs], K, V, sm_scale)
+            out[b, t_exact, h * gs:(h + 1) * gs] = o[t_exact]
+            lse[b, h * gs:(h + 1) * gs, t_exact] = s[:, t_exact]
     return out, lse

@@ -115,3 +115,48 @@ def test_draft_ignores_low_nibbles():
     t2, _ = attention.attend(rep, q, "target", 0.125)
     assert np.array_equal(a, b)
     assert np.abs(t - t2).max() > 1e-4
+
+
+def test_exact_substitution_pins():
+    """attend_exact: nothing selected == attend; every quantized token
+    replaced by its original value == SDPA over the original tokens for the
+    substituted row, other rows unchanged; a token replaced by its own
+    dequantized value (an fp16 number here) changes nothing."""
+    B, H, Hq, d, G, Gv, R, L, T = 1, 2, 8, 64, 32, 32, 32, 200, 2
+    rep, K, V = _build(B, H, d, G, Gv, 2, R, L, seed=5)
+    n_q = rep.n_q
+    q = np.random.default_rng(6).standard_normal((B, T, Hq, d)).astype(np.float16)
+    base, base_lse = attention.attend(rep, q, "target", 0.125)
+    none = -np.ones((B, H, 3), np.int64)
+    z = np.zeros((B, H, 3, d), np.float16)
+    o, s = attention.attend_exact(rep, q, "target", 0.125, none, z, z)
+    assert np.array_equal(o, base) and np.array_equal(s, base_lse)
+    # every quantized token replaced by the original fp16 token
+    idx = np.tile(np.arange(n_q), (B, H, 1))
+    kx = np.transpose(K[:, :n_q], (0, 2, 1, 3))
+    vx = np.transpose(V[:, :n_q], (0, 2, 1, 3))
+    o, s = attention.attend_exact(rep, q, "target", 0.125, idx, kx, vx, t_exact=0)
+    Kt = np.transpose(K, (0, 2, 1, 3)).astype(np.float64)
+    Vt = np.transpose(V, (0, 2, 1, 3)).astype(np.float64)
+    ref, ref_lse = _sdpa(q, Kt, Vt, H, 0.125)
+    assert np.abs(o[:, 0] - ref[:, 0]).max() < 1e-12
+    assert np.abs(s[:, :, 0] - ref_lse[:, :, 0]).max() < 1e-12
+    assert np.array_equal(o[:, 1], base[:, 1]) and np.array_equal(s[:, :, 1], base_lse[:, :, 1])
+    assert np.abs(o[:, 0] - base[:, 0]).max() > 1e-3     # 2-bit codes do differ
+    # substituting a token by its own dequantized value: pick tokens whose
+    # dequantized K and V rows are exactly fp16 numbers
+    Kq = quant.dequant(rep.kq[0, 0], rep.ks[0, 0], rep.kz[0, 0], "key", G)
+    Vq = quant.dequant(rep.vq[0, 0], rep.vs[0, 0], rep.vz[0, 0], "value", Gv)
+    fits = [j for j in range(n_q)
+            if (Kq[j].astype(np.float16).astype(np.float64) == Kq[j]).all()
+            and (Vq[j].astype(np.float16).astype(np.float64) == Vq[j]).all()]
+    assert len(fits) >= 1
+    sel = np.array(fits[:4])
+    idx1 = -np.ones((B, H, len(sel)), np.int64)
+    idx1[0, 0] = sel
+    k1 = np.zeros((B, H, len(sel), d), np.float16)
+    v1 = np.zeros_like(k1)
+    k1[0, 0] = Kq[sel].astype(np.float16)
+    v1[0, 0] = Vq[sel].astype(np.float16)
+    o, s = attention.attend_exact(rep, q, "target", 0.125, idx1, k1, v1)
+    assert np.abs(o - base).max() < 1e-13 and np.abs(s - base_lse).max() < 1e-13
