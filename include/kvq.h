@@ -26,7 +26,9 @@
  * kv_attn_verify (split-K attention over the quantized prefix plus the
  * fp16 residual buffer, merged by log-sum-exp) and kv_topk (per-kv-head
  * top-k over low-bit scores).  kv_dequant_gather rebuilds fp16 rows of a
- * requested token subset.  The rest is host-side bookkeeping.
+ * requested token subset; kv_fetch_rows copies rows of a host-resident fp16
+ * copy and kv_attn_verify_exact substitutes them for one query row.  The
+ * rest is host-side bookkeeping.
  *
  * Conventions for every call
  *   - Ownership: the caller owns every buffer (host struct and device
@@ -160,11 +162,12 @@ int kv_quant_append(kvq_cache* c, const void* k_new, const void* v_new, int n,
  * Host only. */
 int kv_rollback(kvq_cache* c, int m);
 
-/* Workspace bytes kv_attn_verify needs for this cache at any fill level:
- * one fp32 partial (m, l, o for up to 32 rows) per split of every block,
- * for as many splits as the launcher may choose on a device with up to 512
- * resident workgroup slots (it uses fewer on larger devices).  0 if the
- * shape is invalid.  Host only. */
+/* Workspace bytes kv_attn_verify (and kv_attn_verify_exact) needs for this
+ * cache at any fill level: one fp32 partial (m, l, o for up to 32 rows) per
+ * split of every block, for as many splits as the launcher may choose on a
+ * device with up to 512 resident workgroup slots (it uses fewer on larger
+ * devices), plus one spare slot per block for the substitution partial.
+ * 0 if the shape is invalid.  Host only. */
 size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq);
 
 /* Speculative verify / draft attention ([QS] Approach; [SC] Approach for
@@ -189,6 +192,27 @@ size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq);
 int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq, int path,
                    float sm_scale, void* out, float* lse, void* ws,
                    size_t ws_bytes, void* stream);
+
+/* Verify / draft attention with exact substitution for one query row
+ * ([SC] Approach: the KV pairs the speculative token ranks highest are
+ * fetched in full precision and used for the output token).  Same as
+ * kv_attn_verify (same arguments, workspace and result layout), except that
+ * query row t_exact (0 <= t_exact < T) reads the fp16 values
+ * k_exact/v_exact[b][kvh][i] instead of the quantized ones at the
+ * positions idx[b][kvh][i], i < n; the other rows are unchanged.
+ *   idx: device int32 [B][Hkv][n]; each block's entries must be distinct
+ *        (as kv_topk returns them); entries outside [0, n_q) are skipped
+ *        (kv_topk's -1 padding).
+ *   k_exact, v_exact: device fp16 [B][Hkv][n][d] (e.g. from kv_fetch_rows).
+ * One more launch than kv_attn_verify: the substitution partial is computed
+ * into a spare workspace slot and enters the same log-sum-exp merge, so a
+ * fetched token's quantized term is removed and its exact term added.
+ * Requires 0 <= n <= 256. */
+int kv_attn_verify_exact(const kvq_cache* c, const void* q, int T, int Hq,
+                         int path, float sm_scale, int t_exact,
+                         const int32_t* idx, int n, const void* k_exact,
+                         const void* v_exact, void* out, float* lse, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /* Workspace bytes kv_topk needs for this cache at any fill level. */
 size_t kv_topk_workspace_bytes(const kvq_cache* c, int Hq, int k);
@@ -227,6 +251,23 @@ int kv_topk(const kvq_cache* c, const void* q_spec, int Hq, int path, int k,
  * workspace.  Requires 0 <= n <= 2^24. */
 int kv_dequant_gather(const kvq_cache* c, const int32_t* idx, int n, int path,
                       void* k_out, void* v_out, void* stream);
+
+/* Fetch rows of a full-precision copy of the cache held in host memory
+ * ([SC] Approach: the full KV stays off the GPU; the pairs the speculative
+ * token selects are fetched).  host_k, host_v: fp16 [B][Hkv][host_len][d],
+ * in pinned host memory the device can read (hipHostMalloc, or torch
+ * tensors with pin_memory), each B*Hkv*host_len*d halves; the call looks
+ * up their device addresses (hipPointerGetAttributes) and returns
+ * KVQ_EINVAL for memory the device cannot read.  For every block and i < n,
+ * with
+ * p = idx[b][kvh][i] (device int32 [B][Hkv][n]): k_out/v_out[b][kvh][i] =
+ * host row p, or fp16 NaN rows when p is outside [0, host_len).  k_out,
+ * v_out: device fp16 [B][Hkv][n][d].  Only the cache's shape fields are
+ * used.  Enqueue it on a second stream to overlap the transfer with other
+ * work.  Requires 0 <= n <= 2^24. */
+int kv_fetch_rows(const kvq_cache* c, const void* host_k, const void* host_v,
+                  int64_t host_len, const int32_t* idx, int n, void* k_out,
+                  void* v_out, void* stream);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* kv_last_error(void);

@@ -2,8 +2,8 @@
 
 Thin ctypes layer over the C ABI declared in ``include/kvq.h``.  The entry
 points keep the C names (``kv_cache_layout``, ``kv_quant_append``,
-``kv_rollback``, ``kv_attn_verify``, ``kv_topk``, ``kv_dequant_gather`` and
-the workspace sizers);
+``kv_rollback``, ``kv_attn_verify``, ``kv_topk``, ``kv_dequant_gather``,
+``kv_attn_verify_exact``, ``kv_fetch_rows`` and the workspace sizers);
 this module only checks tensor shapes/dtypes, passes device pointers and the
 current HIP stream, and turns non-zero return codes into ``KvqError``.  All
 computation happens in the HIP kernels of ``libkvq.so``; PyTorch is used for
@@ -23,7 +23,8 @@ __all__ = [
     "KVQ_TARGET", "KVQ_DRAFT4", "KvqError", "KvqCacheStruct", "lib",
     "kv_cache_layout", "kv_quant_append", "kv_rollback",
     "kv_attn_workspace_bytes", "kv_attn_verify", "kv_topk_workspace_bytes",
-    "kv_topk", "kv_dequant_gather", "kv_last_error", "QuantKVCache", "LIB_PATH",
+    "kv_topk", "kv_dequant_gather", "kv_attn_verify_exact", "kv_fetch_rows",
+    "kv_last_error", "QuantKVCache", "HostMirror", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -89,10 +90,14 @@ def lib() -> ctypes.CDLL:
     L.kv_topk_workspace_bytes.restype = sz
     L.kv_topk.argtypes = [P, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     L.kv_dequant_gather.argtypes = [P, vp, i32, i32, vp, vp, vp]
+    L.kv_attn_verify_exact.argtypes = [P, vp, i32, i32, i32, f32, i32, vp, i32,
+                                       vp, vp, vp, vp, vp, sz, vp]
+    L.kv_fetch_rows.argtypes = [P, vp, vp, ctypes.c_int64, vp, i32, vp, vp, vp]
     L.kv_last_error.argtypes = []
     L.kv_last_error.restype = ctypes.c_char_p
     for name in ("kv_cache_layout", "kv_quant_append", "kv_rollback",
-                 "kv_attn_verify", "kv_topk", "kv_dequant_gather"):
+                 "kv_attn_verify", "kv_topk", "kv_dequant_gather",
+                 "kv_attn_verify_exact", "kv_fetch_rows"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -161,6 +166,22 @@ def kv_dequant_gather(c: KvqCacheStruct, idx, n: int, path, k_out, v_out,
     _check(lib().kv_dequant_gather(
         ctypes.byref(c), _ptr(idx), n, _path(path), _ptr(k_out), _ptr(v_out),
         _stream(stream)))
+
+
+def kv_attn_verify_exact(c: KvqCacheStruct, q, T: int, Hq: int, path,
+                         sm_scale: float, t_exact: int, idx, n: int, k_exact,
+                         v_exact, out, lse, ws, stream=None) -> None:
+    _check(lib().kv_attn_verify_exact(
+        ctypes.byref(c), _ptr(q), T, Hq, _path(path), float(sm_scale), t_exact,
+        _ptr(idx), n, _ptr(k_exact), _ptr(v_exact), _ptr(out), _ptr(lse),
+        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def kv_fetch_rows(c: KvqCacheStruct, host_k, host_v, host_len: int, idx, n: int,
+                  k_out, v_out, stream=None) -> None:
+    _check(lib().kv_fetch_rows(
+        ctypes.byref(c), _ptr(host_k), _ptr(host_v), host_len, _ptr(idx), n,
+        _ptr(k_out), _ptr(v_out), _stream(stream)))
 
 
 # ---- torch-owned cache -----------------------------------------------------
@@ -282,6 +303,39 @@ class QuantKVCache:
         kv_attn_verify(self.c, q, T, Hq, path, sm_scale, out, lse, ws, stream)
         return out, lse
 
+    def verify_exact(self, q, idx, k_exact, v_exact, t_exact=0, path="target",
+                     sm_scale=None, out=None, lse=None, ws=None, want_lse=False,
+                     stream=None):
+        """kv_attn_verify_exact: like ``verify``, with query row t_exact
+        reading k_exact/v_exact [B][Hkv][n][d] at positions idx
+        [B][Hkv][n]; returns (out, lse)."""
+        import torch
+        s = self.shape
+        if (q.dtype != torch.float16 or not q.is_cuda or not q.is_contiguous()
+                or q.dim() != 4 or q.shape[0] != s.B or q.shape[3] != s.d):
+            raise ValueError("q must be contiguous fp16 CUDA [B][T][Hq][d]")
+        if (idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous()
+                or idx.dim() != 3 or tuple(idx.shape[:2]) != (s.B, s.Hkv)):
+            raise ValueError("idx must be contiguous int32 CUDA [B][Hkv][n]")
+        n = idx.shape[2]
+        for t, name in ((k_exact, "k_exact"), (v_exact, "v_exact")):
+            if (t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous()
+                    or tuple(t.shape) != (s.B, s.Hkv, n, s.d)):
+                raise ValueError(f"{name} must be contiguous fp16 CUDA "
+                                 f"[B][Hkv][n][d]")
+        B, T, Hq, d = q.shape
+        if sm_scale is None:
+            sm_scale = d ** -0.5
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and want_lse:
+            lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+        if ws is None:
+            ws = self.attn_workspace(T, Hq)
+        kv_attn_verify_exact(self.c, q, T, Hq, path, sm_scale, t_exact, idx, n,
+                             k_exact, v_exact, out, lse, ws, stream)
+        return out, lse
+
     def topk_workspace(self, Hq: int, k: int):
         import torch
         n = kv_topk_workspace_bytes(self.c, Hq, k)
@@ -328,4 +382,42 @@ class QuantKVCache:
         if v_out is None:
             v_out = torch.empty(shape, dtype=torch.float16, device=idx.device)
         kv_dequant_gather(self.c, idx, n, path, k_out, v_out, stream)
+        return k_out, v_out
+
+
+class HostMirror:
+    """Full-precision copy of a cache's tokens in pinned host memory, fp16
+    [B][Hkv][L_max][d] for K and V, filled by the caller alongside its
+    appends.  ``fetch`` runs kv_fetch_rows: the rows at positions idx
+    [B][Hkv][n] come back as device fp16 [B][Hkv][n][d]."""
+
+    def __init__(self, shape: Shape, length: int):
+        import torch
+        self.shape, self.length = shape, length
+        dims = (shape.B, shape.Hkv, length, shape.d)
+        self.k = torch.zeros(dims, dtype=torch.float16, pin_memory=True)
+        self.v = torch.zeros(dims, dtype=torch.float16, pin_memory=True)
+
+    def write(self, p0: int, k_tokens, v_tokens) -> None:
+        """Store host fp16 tokens [B][n][Hkv][d] at positions p0.."""
+        import torch
+        n = k_tokens.shape[1]
+        self.k[:, :, p0:p0 + n] = torch.as_tensor(k_tokens).permute(0, 2, 1, 3)
+        self.v[:, :, p0:p0 + n] = torch.as_tensor(v_tokens).permute(0, 2, 1, 3)
+
+    def fetch(self, cache: "QuantKVCache", idx, k_out=None, v_out=None,
+              stream=None):
+        import torch
+        s = self.shape
+        if (idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous()
+                or idx.dim() != 3 or tuple(idx.shape[:2]) != (s.B, s.Hkv)):
+            raise ValueError("idx must be contiguous int32 CUDA [B][Hkv][n]")
+        n = idx.shape[2]
+        shape = (s.B, s.Hkv, n, s.d)
+        if k_out is None:
+            k_out = torch.empty(shape, dtype=torch.float16, device=idx.device)
+        if v_out is None:
+            v_out = torch.empty(shape, dtype=torch.float16, device=idx.device)
+        kv_fetch_rows(cache.c, self.k, self.v, self.length, idx, n, k_out, v_out,
+                      stream)
         return k_out, v_out

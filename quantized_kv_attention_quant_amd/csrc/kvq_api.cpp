@@ -94,8 +94,9 @@ int s_alloc_of(const kvq_cache* c) {
   int64_t s = 4 * cdiv(kSlotsBound, nb);
   const int64_t by_units = cdiv(units_max, kWavesPerGroup);
   if (s > by_units) s = by_units;
-  if (s > kvq::kMaxSplits) s = kvq::kMaxSplits;
-  return s < 1 ? 1 : (int)s;
+  if (s > kvq::kMaxSplits - 1) s = kvq::kMaxSplits - 1;
+  if (s < 1) s = 1;
+  return (int)s + 1;   // one spare slot: the exact-substitution partial
 }
 
 // Two u32 counters per block (split tickets, finished merges), zero between
@@ -181,9 +182,12 @@ KVQ_API size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq) {
          (c->d + 2) * sizeof(float);
 }
 
-KVQ_API int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq,
-                           int path, float sm_scale, void* out, float* lse,
-                           void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// Validation and argument set-up shared by the two attention entry points.
+int attn_setup(const kvq_cache* c, const void* q, int T, int Hq, int path,
+               float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+               kvq::AttnArgs& a) {
   int rc = check_cache(c);
   if (rc) return rc;
   if (!q || !out) return fail(KVQ_EINVAL, "q/out is NULL");
@@ -204,7 +208,6 @@ KVQ_API int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq,
   if (!ws || ws_bytes < need)
     return fail(KVQ_EWORKSPACE, "workspace needs %zu bytes", need);
 
-  kvq::AttnArgs a;
   a.g = kvq::geom_of(c);
   a.p = kvq::ptrs_of(c);
   a.q = (const __half*)q;
@@ -222,8 +225,46 @@ KVQ_API int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq,
   a.S = 0;
   a.s_alloc = s_alloc_of(c);
   a.rows_pad = rows_pad_of(T, Hq, c->Hkv);
+  a.n_exact = -1;
+  a.t_exact = 0;
+  a.idx_exact = nullptr;
+  a.k_exact = a.v_exact = nullptr;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+KVQ_API int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq,
+                           int path, float sm_scale, void* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream) {
+  kvq::AttnArgs a;
+  const int rc = attn_setup(c, q, T, Hq, path, sm_scale, out, lse, ws, ws_bytes, a);
+  if (rc) return rc;
   hipError_t e = kvq::launch_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_attn_verify launch");
+  return KVQ_OK;
+}
+
+KVQ_API int kv_attn_verify_exact(const kvq_cache* c, const void* q, int T, int Hq,
+                                 int path, float sm_scale, int t_exact,
+                                 const int32_t* idx, int n, const void* k_exact,
+                                 const void* v_exact, void* out, float* lse,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  kvq::AttnArgs a;
+  const int rc = attn_setup(c, q, T, Hq, path, sm_scale, out, lse, ws, ws_bytes, a);
+  if (rc) return rc;
+  if (t_exact < 0 || t_exact >= T) return fail(KVQ_EINVAL, "t_exact must be in [0, T)");
+  if (n < 0 || n > kvq::kMaxExact)
+    return fail(KVQ_EINVAL, "n must be in [0, %d]", kvq::kMaxExact);
+  if (n > 0 && (!idx || !k_exact || !v_exact))
+    return fail(KVQ_EINVAL, "idx/k_exact/v_exact is NULL");
+  a.n_exact = n;
+  a.t_exact = t_exact;
+  a.idx_exact = idx;
+  a.k_exact = (const __half*)k_exact;
+  a.v_exact = (const __half*)v_exact;
+  hipError_t e = kvq::launch_attn(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_attn_verify_exact launch");
   return KVQ_OK;
 }
 
@@ -298,6 +339,48 @@ KVQ_API int kv_dequant_gather(const kvq_cache* c, const int32_t* idx, int n,
   a.path = path;
   hipError_t e = kvq::launch_gather(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_dequant_gather launch");
+  return KVQ_OK;
+}
+
+KVQ_API int kv_fetch_rows(const kvq_cache* c, const void* host_k,
+                          const void* host_v, int64_t host_len, const int32_t* idx,
+                          int n, void* k_out, void* v_out, void* stream) {
+  int rc = check_shape(c);
+  if (rc) return rc;
+  if (n < 0 || n > (1 << 24)) return fail(KVQ_EINVAL, "n must be in [0, 2^24]");
+  if (host_len < 0) return fail(KVQ_EINVAL, "host_len must be >= 0");
+  if (n > 0 && (!host_k || !host_v || !idx || !k_out || !v_out))
+    return fail(KVQ_EINVAL, "host_k/host_v/idx/k_out/v_out is NULL");
+  // The host buffers must be pinned allocations the device can read: look
+  // up their device addresses instead of trusting the pointers, so pageable
+  // memory is refused here rather than faulting in the kernel.
+  const void* dev[2] = {nullptr, nullptr};
+  if (n > 0) {
+    const void* hp[2] = {host_k, host_v};
+    for (int i = 0; i < 2; ++i) {
+      hipPointerAttribute_t at;
+      hipError_t e = hipPointerGetAttributes(&at, hp[i]);
+      if (e != hipSuccess || at.type != hipMemoryTypeHost || !at.devicePointer) {
+        (void)hipGetLastError();
+        return fail(KVQ_EINVAL, "host_k/host_v must be pinned host memory the "
+                                "device can read");
+      }
+      dev[i] = at.devicePointer;
+    }
+  }
+  kvq::FetchArgs a;
+  a.host_k = (const __half*)dev[0];
+  a.host_v = (const __half*)dev[1];
+  a.host_len = host_len;
+  a.idx = idx;
+  a.k_out = (__half*)k_out;
+  a.v_out = (__half*)v_out;
+  a.B = c->B;
+  a.Hkv = c->Hkv;
+  a.d = c->d;
+  a.n = n;
+  hipError_t e = kvq::launch_fetch(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_fetch_rows launch");
   return KVQ_OK;
 }
 

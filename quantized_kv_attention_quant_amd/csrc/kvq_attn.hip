@@ -374,6 +374,93 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
     a.lse[((int64_t)b * a.Hq + h) * a.T + t] = (M + __log2f(lsum)) * kLn2;
 }
 
+// Exact substitution, one workgroup per (GQA head hl, kv head, batch): the
+// partial that turns query row t_exact * gs + hl's attention over the
+// quantized cache into attention where the positions idx_exact read the
+// exact fp16 K/V (SpeCache page, Approach: the fetched pairs are used in
+// full precision for the output token).  With logits in the log2 domain,
+// sq_j from the dequantized key and se_j from the exact one:
+//   l = sum_j (2^(se_j - m) - 2^(sq_j - m)),
+//   o = sum_j (2^(se_j - m) v_j - 2^(sq_j - m) v^_j),   m = max_j (sq_j, se_j)
+// written to the spare partial slot S of the block; the log-sum-exp merge of
+// the S + 1 partials then removes each fetched token's quantized term and
+// adds its exact one.  The other query rows of head hl get an empty partial
+// (m = -inf, l = 0, o = 0).  Positions outside [0, n_q) are skipped.
+template <int D, int RP>
+__global__ void __launch_bounds__(256) exact_kernel(const AttnArgs a) {
+  constexpr int NT = 256, NWV = NT / kWave;
+  __shared__ float s_q[D];
+  __shared__ float s_sq[kMaxExact], s_se[kMaxExact];
+  const CacheGeom& g = a.g;
+  const int hl = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int64_t blk = (int64_t)b * g.Hkv + kvh;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int n = a.n_exact, h = kvh * a.gs + hl;
+  const bool draft = a.path == KVQ_DRAFT4;
+  const int64_t pstride = (int64_t)RP * (D + 2);
+  float* po = a.ws + (blk * a.s_alloc + a.S) * pstride;
+  const int32_t* idx = a.idx_exact + blk * n;
+  const __half* ke = a.k_exact + blk * n * D;
+  const __half* ve = a.v_exact + blk * n * D;
+
+  // empty partial for this head's other query rows
+  for (int t = 0; t < a.T; ++t) {
+    if (t == a.t_exact) continue;
+    const int r = t * a.gs + hl;
+    for (int c = tid; c < D; c += NT) po[r * D + c] = 0.f;
+    if (tid == 0) {
+      po[RP * D + r] = -INFINITY;
+      po[RP * D + RP + r] = 0.f;
+    }
+  }
+  if (tid < D)
+    s_q[tid] = __half2float(a.q[(((int64_t)b * a.T + a.t_exact) * a.Hq + h) * D + tid]);
+  __syncthreads();
+  for (int i = wave; i < n; i += NWV) {
+    const int64_t p = idx[i];
+    float dq = 0.f, de = 0.f;
+    const bool ok = p >= 0 && p < a.n_q;
+    if (ok) {
+      for (int c = lane; c < D; c += kWave) {
+        const __half2 sz = key_sz(g, a.p, blk, p, c);
+        const float kq = __high2float(sz) + key_code(g, a.p, blk, p, c, draft) * __low2float(sz);
+        dq += s_q[c] * kq;
+        de += s_q[c] * __half2float(ke[(int64_t)i * D + c]);
+      }
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        dq += __shfl_xor(dq, o);
+        de += __shfl_xor(de, o);
+      }
+    }
+    if (lane == 0) {
+      s_sq[i] = ok ? dq * a.c0 : -INFINITY;
+      s_se[i] = ok ? de * a.c0 : -INFINITY;
+    }
+  }
+  __syncthreads();
+  float m = -INFINITY;
+  for (int i = 0; i < n; ++i) m = fmaxf(m, fmaxf(s_sq[i], s_se[i]));
+  const int row = a.t_exact * a.gs + hl;
+  for (int c = tid; c < D; c += NT) {
+    float o = 0.f, l = 0.f;
+    for (int i = 0; i < n; ++i) {
+      if (s_sq[i] == -INFINITY) continue;
+      const int64_t p = idx[i];
+      const float we = fast_exp2(s_se[i] - m), wq = fast_exp2(s_sq[i] - m);
+      const float2 sz = value_sz(g, a.p, blk, p, c);
+      const float vq = sz.y + value_code(g, a.p, blk, p, c, draft) * sz.x;
+      o += we * __half2float(ve[(int64_t)i * D + c]) - wq * vq;
+      l += we - wq;
+    }
+    po[row * D + c] = o;
+    if (c == 0) {
+      po[RP * D + row] = m;
+      po[RP * D + RP + row] = l;
+    }
+  }
+}
+
 // Dynamic LDS of the split kernel:
 //   stages  [NW][STAGE]       each wave's unit stage
 //   s_q     fp16 [RP][D]      this block's query rows (zero past `rows`)
@@ -1119,7 +1206,8 @@ hipError_t go(AttnArgs a, hipStream_t s) {
   if (occ < 1) return hipErrorInvalidConfiguration;
   const int64_t nb = (int64_t)a.g.B * a.g.Hkv;
   const int64_t units = 2 * cdiv(a.n_r, kTile) + cdiv(a.n_q / kTile, C::TPU);
-  a.S = plan_splits(nb, (int64_t)cus * occ, units, C::NS, a.s_alloc);
+  // the last partial slot of each block stays free for exact substitution
+  a.S = plan_splits(nb, (int64_t)cus * occ, units, C::NS, a.s_alloc - 1);
   a.nq_mod = (int)(a.n_q % a.g.ring);
   const int tpg = a.g.G / kTile;
   a.grp_shift = -1;
@@ -1132,6 +1220,14 @@ hipError_t go(AttnArgs a, hipStream_t s) {
                      dim3(C::NW * kWave), C::LDS, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.n_exact >= 0) {
+    hipLaunchKernelGGL((exact_kernel<D, C::RP>),
+                       dim3((unsigned)a.gs, (unsigned)a.g.Hkv, (unsigned)a.g.B),
+                       dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ++a.S;                       // the merge reads the substitution partial too
+  }
   hipLaunchKernelGGL((merge_kernel<D, C::RP>),
                      dim3((unsigned)a.rows, (unsigned)a.g.Hkv, (unsigned)a.g.B),
                      dim3(256), 0, s, a);

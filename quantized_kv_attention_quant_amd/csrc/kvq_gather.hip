@@ -25,14 +25,6 @@ namespace {
 
 constexpr int kWavesPerGroup = 4;
 
-__device__ inline float dequant(unsigned hi, unsigned lo, bool two, bool draft,
-                                float s, float z) {
-  float code;
-  if (draft) code = 16.f * (float)hi + 7.5f;
-  else code = (float)(two ? (hi << 4) | lo : hi);
-  return __fadd_rn(z, __fmul_rn(code, s));
-}
-
 __global__ void __launch_bounds__(kWavesPerGroup * kWave)
     gather_kernel(const GatherArgs a) {
   const CacheGeom& g = a.g;
@@ -41,7 +33,7 @@ __global__ void __launch_bounds__(kWavesPerGroup * kWave)
   const int i = blockIdx.x * kWavesPerGroup + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (i >= a.n) return;
-  const int d = g.d, w = g.w;
+  const int d = g.d;
   const int64_t p = a.idx[blk * a.n + i];
   __half* ko = a.k_out + (blk * a.n + i) * d;
   __half* vo = a.v_out + (blk * a.n + i) * d;
@@ -66,50 +58,57 @@ __global__ void __launch_bounds__(kWavesPerGroup * kWave)
     return;
   }
 
-  const bool two = g.bits == 8, draft = a.path == KVQ_DRAFT4;
-  const unsigned mask = (1u << w) - 1u;
-  // keys: plane row of token p; scale/zero of its group
-  const uint8_t* krow_hi = a.p.k_hi + blk * g.k_block_bytes + p * g.k_row_bytes;
-  const uint8_t* krow_lo = two ? a.p.k_lo + blk * g.k_block_bytes + p * g.k_row_bytes : nullptr;
-  const __half2* ksz = a.p.k_sz + blk * g.ksz_block + (p / g.G) * d;
-  // values: tile of token p and the token's place in it
-  const int64_t t = p / kTile;
-  const int j = (int)(p % kTile);
-  const int jg = (j % 16) / 4, ji = j % 4, jh = j / 16;
-  const uint32_t* vt_hi =
-      (const uint32_t*)(a.p.v_hi + blk * g.v_block_bytes + t * g.v_tile_bytes);
-  const uint32_t* vt_lo =
-      two ? (const uint32_t*)(a.p.v_lo + blk * g.v_block_bytes + t * g.v_tile_bytes)
-          : nullptr;
-  const int ngv = d / g.Gv;
-  const __half* vsz = (const __half*)(a.p.v_sz + blk * g.vsz_block + t * g.vsz_tile);
-  const int per_byte = 8 / w, per = 4 / w;
-
+  const bool draft = a.path == KVQ_DRAFT4;
   for (int c = lane; c < d; c += kWave) {
-    // key code: byte c / (8/w) of the row, bits w * (c % (8/w))
-    const int kb = c / per_byte, ksh = w * (c % per_byte);
-    const unsigned khi = ((unsigned)krow_hi[kb] >> ksh) & mask;
-    const unsigned klo = two ? ((unsigned)krow_lo[kb] >> ksh) & mask : 0u;
-    const __half2 sz = ksz[c];
-    const float kx = dequant(khi, klo, two, draft, __low2float(sz), __high2float(sz));
+    const __half2 ksz = key_sz(g, a.p, blk, p, c);
+    const float kx = __fadd_rn(__high2float(ksz),
+                               __fmul_rn(key_code(g, a.p, blk, p, c, draft), __low2float(ksz)));
     ko[c] = __float2half_rn(kx);
-    // value code: dword (16 g + r) * (d w / 64) + m / per, bit 16 h + w (4 (m % per) + i)
-    const int r = c % 16, m = c / 16;
-    const int dw = (16 * jg + r) * (d * w / 64) + m / per;
-    const int vsh = 16 * jh + w * (4 * (m % per) + ji);
-    const unsigned vhi = (vt_hi[dw] >> vsh) & mask;
-    const unsigned vlo = two ? (vt_lo[dw] >> vsh) & mask : 0u;
-    // scale / zero: [part][g][i][group][h] halves within the tile
-    const int gg = c / g.Gv;
-    const int so = ((0 * 4 + jg) * 4 + ji) * ngv * 2 + gg * 2 + jh;
-    const int zo = ((1 * 4 + jg) * 4 + ji) * ngv * 2 + gg * 2 + jh;
-    const float vx = dequant(vhi, vlo, two, draft, __half2float(vsz[so]),
-                             __half2float(vsz[zo]));
+    const float2 vsz = value_sz(g, a.p, blk, p, c);
+    const float vx = __fadd_rn(vsz.y, __fmul_rn(value_code(g, a.p, blk, p, c, draft), vsz.x));
     vo[c] = __float2half_rn(vx);
   }
 }
 
+// Rows of a full-precision copy of the cache kept in host memory (SpeCache
+// page, Approach: the full KV stays off the GPU and the pairs the
+// speculative token selects are fetched).  One wave per requested row; each
+// lane moves 16 bytes of K and of V straight from host memory (the buffers
+// are device-accessible pinned allocations), so a request of n rows per
+// block crosses the host link once, as 2 * n * d * 2 bytes per block.
+__global__ void __launch_bounds__(kWavesPerGroup * kWave)
+    fetch_kernel(const FetchArgs a) {
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int64_t blk = (int64_t)b * a.Hkv + kvh;
+  const int i = blockIdx.x * kWavesPerGroup + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (i >= a.n) return;
+  const int d8 = a.d / 8;                       // 16-byte pieces per row
+  const int64_t p = a.idx[blk * a.n + i];
+  uint4* ko = (uint4*)(a.k_out + (blk * a.n + i) * a.d);
+  uint4* vo = (uint4*)(a.v_out + (blk * a.n + i) * a.d);
+  if (lane >= d8) return;
+  if (p < 0 || p >= a.host_len) {
+    const unsigned nan2 = 0x7e007e00u;
+    ko[lane] = make_uint4(nan2, nan2, nan2, nan2);
+    vo[lane] = make_uint4(nan2, nan2, nan2, nan2);
+    return;
+  }
+  const int64_t row = (blk * a.host_len + p) * a.d;
+  ko[lane] = ((const uint4*)(a.host_k + row))[lane];
+  vo[lane] = ((const uint4*)(a.host_v + row))[lane];
+}
+
 }  // namespace
+
+hipError_t launch_fetch(const FetchArgs& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fetch_kernel,
+                     dim3((unsigned)cdiv(a.n, kWavesPerGroup), (unsigned)a.Hkv,
+                          (unsigned)a.B),
+                     dim3(kWavesPerGroup * kWave), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;

@@ -13,6 +13,7 @@ namespace kvq {
 constexpr int kTile = 32;       // tokens per V tile / ring tile
 constexpr int kWave = 64;       // CDNA wavefront width
 constexpr int kMaxSplits = 1024;   // split partials per block; their weights fit the merge LDS
+constexpr int kMaxExact = 256;     // positions per block in an exact substitution
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) {
   return (a + b - 1) / b;
@@ -77,6 +78,59 @@ __host__ __device__ inline int vres_index(int j, int c, int d) {
   return (16 * g + r) * (d / 2) + 8 * m + 2 * i + h;
 }
 
+// ---- one quantized element, read straight from the device layouts --------
+// Code of channel c of quantized token pos (< n_q) of block blk, as the path
+// reads it: every stored bit (q) or the INT4 draft view 16*(q >> 4) + 7.5.
+__device__ inline float code_value(unsigned hi, unsigned lo, bool two, bool draft) {
+  if (draft) return 16.f * (float)hi + 7.5f;
+  return (float)(two ? (hi << 4) | lo : hi);
+}
+
+// Key: byte c / (8/w) of the token's plane row, bits w * (c % (8/w)); its
+// key group's (s, z) pair.
+__device__ inline float key_code(const CacheGeom& g, const CachePtrs& p,
+                                 int64_t blk, int64_t pos, int c, bool draft) {
+  const int per_byte = 8 / g.w, sh = g.w * (c % per_byte);
+  const unsigned mask = (1u << g.w) - 1u;
+  const int64_t row = blk * g.k_block_bytes + pos * g.k_row_bytes + c / per_byte;
+  const unsigned hi = ((unsigned)p.k_hi[row] >> sh) & mask;
+  const unsigned lo = g.bits == 8 ? ((unsigned)p.k_lo[row] >> sh) & mask : 0u;
+  return code_value(hi, lo, g.bits == 8, draft);
+}
+__device__ inline __half2 key_sz(const CacheGeom& g, const CachePtrs& p,
+                                 int64_t blk, int64_t pos, int c) {
+  return p.k_sz[blk * g.ksz_block + (pos / g.G) * g.d + c];
+}
+
+// Value: token j = pos % 32 of its 32-token tile (g = (j%16)/4, i = j%4,
+// h = j/16), channel c (r = c%16, m = c/16): dword (16g + r)*(d w/64) + m/per
+// of the tile, bits 16h + w (4 (m%per) + i), per = 4/w.
+__device__ inline float value_code(const CacheGeom& g, const CachePtrs& p,
+                                   int64_t blk, int64_t pos, int c, bool draft) {
+  const int j = (int)(pos % kTile);
+  const int jg = (j % 16) / 4, ji = j % 4, jh = j / 16, r = c % 16, m = c / 16;
+  const int per = 4 / g.w;
+  const int dw = (16 * jg + r) * (g.d * g.w / 64) + m / per;
+  const int sh = 16 * jh + g.w * (4 * (m % per) + ji);
+  const unsigned mask = (1u << g.w) - 1u;
+  const int64_t tile = blk * g.v_block_bytes + (pos / kTile) * g.v_tile_bytes;
+  const unsigned hi = (((const uint32_t*)(p.v_hi + tile))[dw] >> sh) & mask;
+  const unsigned lo =
+      g.bits == 8 ? (((const uint32_t*)(p.v_lo + tile))[dw] >> sh) & mask : 0u;
+  return code_value(hi, lo, g.bits == 8, draft);
+}
+// The value group's (s, z): halves [part][g][i][group][h] of the tile.
+__device__ inline float2 value_sz(const CacheGeom& g, const CachePtrs& p,
+                                  int64_t blk, int64_t pos, int c) {
+  const int j = (int)(pos % kTile);
+  const int jg = (j % 16) / 4, ji = j % 4, jh = j / 16;
+  const int ngv = g.d / g.Gv, gg = c / g.Gv;
+  const __half* t = (const __half*)(p.v_sz + blk * g.vsz_block + (pos / kTile) * g.vsz_tile);
+  const int so = (jg * 4 + ji) * ngv * 2 + gg * 2 + jh;
+  const int zo = ((4 + jg) * 4 + ji) * ngv * 2 + gg * 2 + jh;
+  return make_float2(__half2float(t[so]), __half2float(t[zo]));
+}
+
 // ---- launchers (defined in the .hip files; return hipError_t) ----------
 
 // Append/flush: see kv_quant_append.  Items [flush_begin, flush_end) are
@@ -113,6 +167,12 @@ struct AttnArgs {
   int rows_pad;     // 16 * row tiles
   int nq_mod;       // n_q mod ring: ring slot of the first residual token
   int grp_shift;    // log2(G / 32) when G / 32 is a power of two, else -1
+  // exact substitution (kv_attn_verify_exact); n_exact < 0: none
+  int n_exact;              // positions per block in idx_exact
+  int t_exact;              // the query row that reads the exact values
+  const int32_t* idx_exact; // [B][Hkv][n_exact] quantized positions (-1: skip)
+  const __half* k_exact;    // [B][Hkv][n_exact][d]
+  const __half* v_exact;    // [B][Hkv][n_exact][d]
 };
 // Splits per block for nb blocks on `slots` resident workgroup slots, with
 // `units` units of work per block, nw waves per workgroup, at most cap.
@@ -131,6 +191,18 @@ struct GatherArgs {
   int path;             // KVQ_TARGET / KVQ_DRAFT4
 };
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+
+// Rows of host-resident fp16 K/V: see kv_fetch_rows.
+struct FetchArgs {
+  const __half* host_k;   // [B][Hkv][host_len][d], device-accessible host memory
+  const __half* host_v;
+  int64_t host_len;
+  const int32_t* idx;     // [B][Hkv][n]
+  __half* k_out;          // [B][Hkv][n][d]
+  __half* v_out;
+  int B, Hkv, d, n;
+};
+hipError_t launch_fetch(const FetchArgs& a, hipStream_t s);
 
 struct TopkArgs {
   CacheGeom g;

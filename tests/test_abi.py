@@ -29,7 +29,7 @@ def test_exports_match_header():
     assert names == {"kv_cache_layout", "kv_quant_append", "kv_rollback",
                      "kv_attn_workspace_bytes", "kv_attn_verify",
                      "kv_topk_workspace_bytes", "kv_topk", "kv_dequant_gather",
-                     "kv_last_error"}
+                     "kv_attn_verify_exact", "kv_fetch_rows", "kv_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", kq.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
