@@ -219,6 +219,85 @@ def comparators(w, seed, K, V, caches, q_draft, q_verify, k_new, v_new,
     }
 
 
+def specache_pipeline(seed, steps=30):
+    """The SpeCache-style prefetch path at the batched 32K 2-bit size (B=36,
+    Hq=32, Hkv=8, d=128, G=Gv=R=32, T=2: output token + speculative token):
+      kv_topk           top-64 positions per kv head from the speculative
+                        token's 2-bit scores
+      kv_fetch_rows     those rows' fp16 K and V from a pinned host copy
+      kv_attn_verify_exact  T=2 with the output token reading them exactly
+    beside plain kv_attn_verify on the same cache.  K/V are a seeded device
+    draw (only shapes matter for the timing); HIP events on the launch
+    stream, each call timed alone."""
+    import torch
+    import kvq_synth as synth
+    import quantized_kv_attention_quant_amd as kq
+    w = synth.WORKLOADS["specache_2bit"]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 11)
+    shape = kq.Shape(B=w.B, Hkv=w.Hkv, d=w.d, G=w.G, Gv=w.Gv, bits=w.bits,
+                     R=w.R, L_max=w.L, max_append=32)
+    cache = kq.QuantKVCache(shape, device=dev)
+    mirror = kq.HostMirror(shape, w.L)
+    T = 2
+    for lo, hi in ((0, w.L - T), (w.L - T, w.L)):
+        K = torch.randn((w.B, hi - lo, w.Hkv, w.d), generator=g, device=dev).half()
+        V = torch.randn((w.B, hi - lo, w.Hkv, w.d), generator=g, device=dev).half()
+        cache.append(K, V)
+        mirror.k[:, :, lo:hi].copy_(K.permute(0, 2, 1, 3).cpu())
+        mirror.v[:, :, lo:hi].copy_(V.permute(0, 2, 1, 3).cpu())
+        del K, V
+    q = torch.from_numpy(synth.queries(w, seed + 3, T)).to(dev)
+    q_spec = q[:, T - 1].contiguous()
+    k = w.topk
+    idx = torch.empty((w.B, w.Hkv, k), dtype=torch.int32, device=dev)
+    kx = torch.empty((w.B, w.Hkv, k, w.d), dtype=torch.float16, device=dev)
+    vx = torch.empty_like(kx)
+    out = torch.empty_like(q)
+    tws = cache.topk_workspace(w.Hq, k)
+    aws = cache.attn_workspace(T, w.Hq)
+    torch.cuda.synchronize()
+    calls = {
+        "topk": lambda: cache.topk(q_spec, k, idx=idx, ws=tws),
+        "fetch": lambda: mirror.fetch(cache, idx, kx, vx),
+        "verify_exact": lambda: cache.verify_exact(q, idx, kx, vx, t_exact=0,
+                                                   out=out, ws=aws),
+        "verify": lambda: cache.verify(q, out=out, ws=aws),
+    }
+    ts = {name: [] for name in calls}
+    for i in range(steps + 3):
+        for name, fn in calls.items():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            if i >= 3:
+                ts[name].append((e0, e1))
+    torch.cuda.synchronize()
+    us = {n: float(np.median([a.elapsed_time(b) for a, b in v])) * 1e3
+          for n, v in ts.items()}
+    fetch_bytes = 2 * w.B * w.Hkv * k * w.d * 2
+    verify_bytes = w.B * algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv,
+                                           cache.n_q, cache.n_r, T, w.bits)
+    res = {
+        "workload": "SpeCache-style batched 2-bit cache: B=36 Hq=32 Hkv=8 "
+                    "d=128 L=32768 G=Gv=R=32, T=2, top-64 per kv head",
+        "topk_us": round(us["topk"], 3),
+        "fetch_us": round(us["fetch"], 3),
+        "fetch_host_gbps": round(fetch_bytes / (us["fetch"] * 1e-6) / 1e9, 2),
+        "verify_exact_us": round(us["verify_exact"], 3),
+        "verify_us": round(us["verify"], 3),
+        "verify_gbps": round(verify_bytes / (us["verify"] * 1e-6) / 1e9, 1),
+        "pipeline_us": round(us["topk"] + us["fetch"] + us["verify_exact"], 3),
+    }
+    del cache, mirror
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,7 +306,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true",
-                    help="skip the fp16-comparator and gather measurements")
+                    help="skip the fp16-comparator, gather and prefetch "
+                         "measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (profiling scale)")
     args = ap.parse_args()
@@ -361,6 +441,7 @@ def main():
                                              / ku["verify_int8_t7"], 3)
         comp["int4_vs_fp16_speedup"] = round(comp["fp16_decode_t1_us"]
                                              / ku["draft_int4_t1"], 3)
+        comp["specache_prefetch"] = specache_pipeline(args.seed)
         res["comparators"] = comp
     if args.calibrate_copy:
         calibrate_copy()

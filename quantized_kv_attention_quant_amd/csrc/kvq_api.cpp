@@ -99,12 +99,6 @@ int s_alloc_of(const kvq_cache* c) {
   return (int)s + 1;   // one spare slot: the exact-substitution partial
 }
 
-// Two u32 counters per block (split tickets, finished merges), zero between
-// calls.
-size_t ticket_bytes(const kvq_cache* c) {
-  return (size_t)round_up((int64_t)c->B * c->Hkv * 8, 256);
-}
-
 }  // namespace
 
 KVQ_API int kv_cache_layout(kvq_cache* c) {
@@ -271,8 +265,7 @@ KVQ_API int kv_attn_verify_exact(const kvq_cache* c, const void* q, int T, int H
 KVQ_API size_t kv_topk_workspace_bytes(const kvq_cache* c, int Hq, int k) {
   if (check_shape(c) || Hq < 1 || k < 1) return 0;
   const int64_t chunks = cdiv(c->L_max, kTopkChunk);
-  return ticket_bytes(c) +
-         (size_t)c->B * c->Hkv * chunks * k * sizeof(unsigned long long);
+  return (size_t)c->B * c->Hkv * chunks * k * sizeof(unsigned long long);
 }
 
 KVQ_API int kv_topk(const kvq_cache* c, const void* q_spec, int Hq, int path,
@@ -300,8 +293,7 @@ KVQ_API int kv_topk(const kvq_cache* c, const void* q_spec, int Hq, int path,
   a.q = (const __half*)q_spec;
   a.idx = idx;
   a.key = key;
-  a.tickets = (unsigned*)ws;
-  a.cand = (unsigned long long*)((char*)ws + ticket_bytes(c));
+  a.cand = (unsigned long long*)ws;
   a.n_q = c->n_q;
   a.Hq = Hq;
   a.gs = gs;

@@ -211,7 +211,6 @@ struct TopkArgs {
   int32_t* idx;
   float* key;
   unsigned long long* cand;  // [B*Hkv][chunks][k]
-  unsigned* tickets;
   int64_t n_q;
   int Hq, gs, k, path;
   int chunk;         // tokens per workgroup

@@ -11,12 +11,20 @@
 // built with -ffp-contract=off (and the pragma below): no product is fused
 // into the following sum.
 //
-// Grid: chunks x Hkv x B, 256 threads; a workgroup scores a chunk of 1024
-// tokens (4 per thread), turns each key into a 64-bit composite
-// (order-preserving key bits << 32 | ~index) so that one unsigned compare
-// orders by key descending then index ascending, sorts the chunk in LDS
-// (bitonic) and writes its best k.  The last workgroup of the block (atomic
-// ticket, self-resetting) merges the chunk candidates the same way.
+// Two launches:
+//   score_kernel, grid chunks x Hkv x B, 256 threads: a workgroup scores a
+//     chunk of 1024 tokens, 4 per thread, with q and the chunk's (s, z)
+//     pairs staged in LDS; a token's sum runs over c = 0..d-1 in order.
+//     Each key becomes a 64-bit composite (order-preserving key bits << 32 |
+//     ~index), so one unsigned compare orders by key descending then index
+//     ascending.  The chunk is sorted by a bitonic network over the 4
+//     composites each thread holds in registers: compare partners in the
+//     same thread or wave are exchanged by lane shuffles, and only the 3
+//     stages whose partners sit in another wave go through LDS.  The
+//     chunk's best k go to the workspace.
+//   merge_kernel, grid Hkv x B: sorts a block's chunk candidates in LDS and
+//     writes the best k.  The kernel boundary makes the candidates visible;
+//     no fence or counter is needed.
 #include "kvq_internal.h"
 
 #pragma clang fp contract(off)
@@ -25,7 +33,9 @@ namespace kvq {
 namespace {
 
 constexpr int NT = 256;
-constexpr int kChunk = 1024;
+constexpr int kChunk = 1024;          // tokens per scoring workgroup
+constexpr int TPT = kChunk / NT;      // consecutive tokens per thread
+static_assert(TPT == 4, "a thread holds 4 composites");
 
 __device__ __forceinline__ unsigned long long composite(float key, int64_t j) {
   unsigned u = __float_as_uint(key);
@@ -59,96 +69,191 @@ __device__ void sort_desc(unsigned long long* v, int n) {
   }
 }
 
+__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x,
+                                                         int m) {
+  const unsigned lo = __shfl_xor((unsigned)x, m);
+  const unsigned hi = __shfl_xor((unsigned)(x >> 32), m);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Descending bitonic sort of the workgroup's NT * 4 composites, element
+// 4 * tid + m in e[m].  Element i meets i ^ j at stage (k, j); the pair is
+// put in descending order when (i & k) == 0, ascending otherwise (the same
+// network as sort_desc).
+__device__ void sort_regs_desc(unsigned long long (&e)[TPT],
+                               unsigned long long* lds) {
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= NT * TPT; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < TPT) {                      // both elements in this thread
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) {
+          const int mp = m ^ j;
+          if (mp > m) {
+            const int i = TPT * tid + m;
+            const bool desc = (i & k) == 0;
+            const unsigned long long x = e[m], y = e[mp];
+            if (desc ? (x < y) : (x > y)) {
+              e[m] = y;
+              e[mp] = x;
+            }
+          }
+        }
+        continue;
+      }
+      const int tj = j / TPT;             // partner thread: tid ^ tj
+      const bool lower = (tid & tj) == 0; // this thread holds the lower index
+      unsigned long long y[TPT];
+      if (tj < kWave) {
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) y[m] = shfl_xor64(e[m], tj);
+      } else {
+        __syncthreads();                  // earlier readers of lds are done
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) lds[TPT * tid + m] = e[m];
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) y[m] = lds[TPT * (tid ^ tj) + m];
+      }
+#pragma unroll
+      for (int m = 0; m < TPT; ++m) {
+        const int i = TPT * tid + m;
+        const bool desc = (i & k) == 0;   // same for both (j < k)
+        // the lower index keeps the larger in a descending pair
+        const bool keep_max = desc == lower;
+        const unsigned long long x = e[m];
+        e[m] = keep_max ? (x > y[m] ? x : y[m]) : (x < y[m] ? x : y[m]);
+      }
+    }
+  }
+}
+
+// Code of channel cc of a code dword (hi plane; lo plane for 8-bit), per
+// path, as a float.
+template <int BITS, int PATH>
+__device__ __forceinline__ float code_of(unsigned h, unsigned l, int cc) {
+  if constexpr (BITS == 8) {
+    const unsigned hn = (h >> (4 * cc)) & 15u;
+    if constexpr (PATH == KVQ_DRAFT4) {
+      return (float)(16u * hn) + 7.5f;
+    } else {
+      return (float)(16u * hn + ((l >> (4 * cc)) & 15u));
+    }
+  } else if constexpr (BITS == 2) {
+    return (float)((h >> (2 * cc)) & 3u);
+  } else {
+    return (float)((h >> cc) & 1u);
+  }
+}
+
 template <int BITS, int PATH, int D, int GS>
-__global__ void __launch_bounds__(NT) topk_kernel(const TopkArgs a) {
-  __shared__ float s_q[GS * D];
-  __shared__ unsigned long long s_c[2 * kChunk];
-  __shared__ int s_flag;
+__global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
+  constexpr int NGC = kChunk / 32 + 1;           // key groups a chunk can touch
+  constexpr int SZR = D + 1;                     // padded row: groups in distinct banks
+  __shared__ float s_q[D][GS];                   // q of the group, channel-major
+  __shared__ float2 s_sz[NGC * SZR];             // (s, z) of the chunk's key groups
+  __shared__ unsigned long long s_x[NT * TPT];   // cross-wave sort exchange
   const CacheGeom& g = a.g;
   const int b = blockIdx.z, kvh = blockIdx.y, chunk = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
 
-  for (int e = tid; e < GS * D; e += NT)
-    s_q[e] = __half2float(a.q[((int64_t)b * a.Hq + kvh * GS + e / D) * D + e % D]);
+  for (int e = tid; e < GS * D; e += NT) {
+    const int h = e / D, c = e % D;
+    s_q[c][h] = __half2float(a.q[((int64_t)b * a.Hq + kvh * GS + h) * D + c]);
+  }
+  // the key groups the chunk's tokens fall in (G is a multiple of 32, so a
+  // chunk touches at most 1024/32 + 1); groups past n_q are not read
+  const int64_t c0 = (int64_t)chunk * kChunk;
+  const int64_t gi0 = c0 / g.G;
+  const int ng = (int)((c0 + kChunk - 1) / g.G - gi0) + 1;
+  const __half2* ksz = a.p.k_sz + blk * g.ksz_block;
+  for (int e = tid; e < ng * D; e += NT) {
+    const int gi = e / D, c = e % D;
+    s_sz[gi * SZR + c] = (gi0 + gi) * g.G < a.n_q
+                             ? __half22float2(ksz[(gi0 + gi) * D + c])
+                             : make_float2(0.f, 0.f);
+  }
   __syncthreads();
 
   constexpr int W = BITS == 8 ? 4 : BITS;
-  constexpr int ROW = D * W / 8;
+  constexpr int NDW = D * W / 32;                // code dwords per plane row
+  constexpr int CPD = 32 / W;                    // channels per code dword
+  constexpr bool LO = BITS == 8 && PATH != KVQ_DRAFT4;
   const uint8_t* kh = a.p.k_hi + blk * g.k_block_bytes;
-  const uint8_t* kl = BITS == 8 ? a.p.k_lo + blk * g.k_block_bytes : nullptr;
-  const __half2* ksz = a.p.k_sz + blk * g.ksz_block;
+  const uint8_t* kl = LO ? a.p.k_lo + blk * g.k_block_bytes : nullptr;
 
-  for (int e = tid; e < kChunk; e += NT) {
-    const int64_t j = (int64_t)chunk * kChunk + e;
-    unsigned long long comp = 0ull;   // below every real key
+  // thread t scores tokens t, t + 256, t + 512, t + 768 of the chunk (one
+  // code row load per wave is one contiguous span)
+  unsigned long long comp[TPT];
+#pragma unroll 1
+  for (int m = 0; m < TPT; ++m) {
+    const int64_t j = c0 + m * NT + tid;
+    unsigned long long cm = 0ull;                // below every real key
     if (j < a.n_q) {
-      constexpr int NDW = ROW / 4;
-      unsigned hw[NDW], lw[BITS == 8 ? NDW : 1];
+      unsigned hw[NDW], lw[LO ? NDW : 1];
 #pragma unroll
       for (int x = 0; x < NDW / 4; ++x) {
-        const uint4 v = ((const uint4*)(kh + j * ROW))[x];
+        const uint4 v = ((const uint4*)(kh + j * (NDW * 4)))[x];
         hw[4 * x] = v.x; hw[4 * x + 1] = v.y; hw[4 * x + 2] = v.z; hw[4 * x + 3] = v.w;
-        if constexpr (BITS == 8) {
-          const uint4 u = ((const uint4*)(kl + j * ROW))[x];
+        if constexpr (LO) {
+          const uint4 u = ((const uint4*)(kl + j * (NDW * 4)))[x];
           lw[4 * x] = u.x; lw[4 * x + 1] = u.y; lw[4 * x + 2] = u.z; lw[4 * x + 3] = u.w;
         }
       }
-      const __half2* sz = ksz + (j / g.G) * D;
+      const float2* sz = s_sz + (int)(j / g.G - gi0) * SZR;
       float acc[GS];
 #pragma unroll
       for (int h = 0; h < GS; ++h) acc[h] = 0.f;
+      // channels in order, one code dword per iteration; the dwords move
+      // down a register window so the loop stays rolled (unrolled, every
+      // channel's LDS reads would be hoisted and hold the registers)
+#pragma unroll 1
+      for (int x = 0; x < NDW; ++x) {
+        const unsigned h0 = hw[0], l0 = LO ? lw[0] : 0u;
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        float code;
-        if constexpr (BITS == 8) {
-          const unsigned hn = (hw[c / 8] >> (4 * (c % 8))) & 15u;
-          if constexpr (PATH == KVQ_DRAFT4) {
-            code = (float)(16u * hn) + 7.5f;
-          } else {
-            const unsigned ln = (lw[c / 8] >> (4 * (c % 8))) & 15u;
-            code = (float)(16u * hn + ln);
-          }
-        } else if constexpr (BITS == 2) {
-          code = (float)((hw[c / 16] >> (2 * (c % 16))) & 3u);
-        } else {
-          code = (float)((hw[c / 32] >> (c % 32)) & 1u);
+        for (int i = 0; i + 1 < NDW; ++i) {
+          hw[i] = hw[i + 1];
+          if constexpr (LO) lw[i] = lw[i + 1];
         }
-        const float2 p = __half22float2(sz[c]);   // (s, z)
-        const float kc = p.y + code * p.x;
 #pragma unroll
-        for (int h = 0; h < GS; ++h) acc[h] = acc[h] + s_q[h * D + c] * kc;
+        for (int cc = 0; cc < CPD; ++cc) {
+          const int c = x * CPD + cc;
+          const float code = code_of<BITS, PATH>(h0, l0, cc);
+          const float2 p = sz[c];                // (s, z)
+          const float kc = p.y + code * p.x;
+#pragma unroll
+          for (int h = 0; h < GS; ++h) acc[h] = acc[h] + s_q[c][h] * kc;
+        }
       }
       float key = acc[0];
 #pragma unroll
       for (int h = 1; h < GS; ++h) key = fmaxf(key, acc[h]);
       key = key + 0.f;
-      comp = composite(key, j);
+      cm = composite(key, j);
     }
-    s_c[e] = comp;
+    comp[m] = cm;
   }
-  __syncthreads();
-  sort_desc(s_c, kChunk);
+
+  sort_regs_desc(comp, s_x);
   unsigned long long* cand = a.cand + (blk * a.chunks + chunk) * a.k;
-  for (int i = tid; i < a.k; i += NT) cand[i] = s_c[i];
+#pragma unroll
+  for (int m = 0; m < TPT; ++m)
+    if (TPT * tid + m < a.k) cand[TPT * tid + m] = comp[m];
+}
 
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&a.tickets[blk], 1u);
-    s_flag = prev == (unsigned)(a.chunks - 1);
-  }
-  __syncthreads();
-  if (!s_flag) return;
-  __threadfence();
-
-  // Merge: keep the best k in s_c[0, k); refill the rest in batches.
+// One workgroup per block: the best k of the chunks' candidates.
+__global__ void __launch_bounds__(NT) merge_kernel(const TopkArgs a) {
+  __shared__ unsigned long long s_c[2 * kChunk];
+  const int b = blockIdx.y, kvh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t blk = (int64_t)b * a.g.Hkv + kvh;
+  // keep the best k in s_c[0, k); refill the rest in batches
   const unsigned long long* all = a.cand + blk * a.chunks * a.k;
   const int total = a.chunks * a.k;
   const int cap = 2 * kChunk;
-  int taken = 0;
   for (int i = tid; i < cap; i += NT) s_c[i] = i < total ? all[i] : 0ull;
-  taken = total < cap ? total : cap;
+  int taken = total < cap ? total : cap;
   __syncthreads();
   sort_desc(s_c, cap);
   while (taken < total) {
@@ -167,13 +272,15 @@ __global__ void __launch_bounds__(NT) topk_kernel(const TopkArgs a) {
     idx[i] = valid ? (int32_t)(0xFFFFFFFFu - (unsigned)(c & 0xFFFFFFFFu)) : -1;
     if (key) key[i] = valid ? key_of(c) : -INFINITY;
   }
-  if (tid == 0) a.tickets[blk] = 0u;
 }
 
 template <int BITS, int PATH, int D, int GS>
 hipError_t go(const TopkArgs& a, hipStream_t s) {
-  dim3 grid(a.chunks, a.g.Hkv, a.g.B);
-  hipLaunchKernelGGL((topk_kernel<BITS, PATH, D, GS>), grid, dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((score_kernel<BITS, PATH, D, GS>),
+                     dim3(a.chunks, a.g.Hkv, a.g.B), dim3(NT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_kernel, dim3(a.g.Hkv, a.g.B), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -196,6 +303,7 @@ hipError_t by_d(const TopkArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  if (a.chunk != kChunk || a.k > NT * TPT) return hipErrorInvalidValue;
   if (a.g.bits == 8)
     return a.path == KVQ_DRAFT4 ? by_d<8, KVQ_DRAFT4>(a, s)
                                 : by_d<8, KVQ_TARGET>(a, s);
