@@ -386,20 +386,26 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
 // the S + 1 partials then removes each fetched token's quantized term and
 // adds its exact one.  The other query rows of head hl get an empty partial
 // (m = -inf, l = 0, o = 0).  Positions outside [0, n_q) are skipped.
+// A wave scores fetched tokens with its lanes over the channels, four
+// tokens in flight at a time; the output pass runs threads over (token
+// subset, channel) so the code and scale loads of many tokens are in flight
+// together, and the subsets meet in LDS.
 template <int D, int RP>
 __global__ void __launch_bounds__(256) exact_kernel(const AttnArgs a) {
-  constexpr int NT = 256, NWV = NT / kWave;
+  constexpr int NT = 256;
+  constexpr int PARTS = NT / D;                  // token subsets in the output pass
   __shared__ float s_q[D];
   __shared__ float s_sq[kMaxExact], s_se[kMaxExact];
+  __shared__ int s_idx[kMaxExact];
+  __shared__ float s_po[PARTS][D], s_pl[PARTS][D];
   const CacheGeom& g = a.g;
   const int hl = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x;
   const int n = a.n_exact, h = kvh * a.gs + hl;
   const bool draft = a.path == KVQ_DRAFT4;
   const int64_t pstride = (int64_t)RP * (D + 2);
   float* po = a.ws + (blk * a.s_alloc + a.S) * pstride;
-  const int32_t* idx = a.idx_exact + blk * n;
   const __half* ke = a.k_exact + blk * n * D;
   const __half* ve = a.v_exact + blk * n * D;
 
@@ -415,48 +421,77 @@ __global__ void __launch_bounds__(256) exact_kernel(const AttnArgs a) {
   }
   if (tid < D)
     s_q[tid] = __half2float(a.q[(((int64_t)b * a.T + a.t_exact) * a.Hq + h) * D + tid]);
+  for (int i = tid; i < n; i += NT) s_idx[i] = a.idx_exact[blk * n + i];
   __syncthreads();
-  for (int i = wave; i < n; i += NWV) {
-    const int64_t p = idx[i];
-    float dq = 0.f, de = 0.f;
-    const bool ok = p >= 0 && p < a.n_q;
-    if (ok) {
-      for (int c = lane; c < D; c += kWave) {
-        const __half2 sz = key_sz(g, a.p, blk, p, c);
-        const float kq = __high2float(sz) + key_code(g, a.p, blk, p, c, draft) * __low2float(sz);
-        dq += s_q[c] * kq;
-        de += s_q[c] * __half2float(ke[(int64_t)i * D + c]);
-      }
+
+  // logits of the dequantized and the exact key: one wave per token, lanes
+  // over channels (coalesced), UT tokens of a wave in flight together
+  constexpr int NWV = NT / kWave, UT = 4;
+  const int wave = tid / kWave, lane = tid % kWave;
+  for (int i0 = wave; i0 < n; i0 += NWV * UT) {
+    float dq[UT], de[UT];
+    bool ok[UT];
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        dq += __shfl_xor(dq, o);
-        de += __shfl_xor(de, o);
+    for (int u = 0; u < UT; ++u) {
+      const int i = i0 + u * NWV;
+      const int64_t p = i < n ? s_idx[i] : -1;
+      ok[u] = p >= 0 && p < a.n_q;
+      dq[u] = de[u] = 0.f;
+      if (ok[u]) {
+#pragma unroll
+        for (int c = lane; c < D; c += kWave) {
+          const __half2 sz = key_sz(g, a.p, blk, p, c);
+          const float kq = __high2float(sz) + key_code(g, a.p, blk, p, c, draft) * __low2float(sz);
+          dq[u] += s_q[c] * kq;
+          de[u] += s_q[c] * __half2float(ke[(int64_t)i * D + c]);
+        }
       }
     }
-    if (lane == 0) {
-      s_sq[i] = ok ? dq * a.c0 : -INFINITY;
-      s_se[i] = ok ? de * a.c0 : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        dq[u] += __shfl_xor(dq[u], o);
+        de[u] += __shfl_xor(de[u], o);
+      }
+      const int i = i0 + u * NWV;
+      if (lane == 0 && i < n) {
+        s_sq[i] = ok[u] ? dq[u] * a.c0 : -INFINITY;
+        s_se[i] = ok[u] ? de[u] * a.c0 : -INFINITY;
+      }
     }
   }
   __syncthreads();
   float m = -INFINITY;
   for (int i = 0; i < n; ++i) m = fmaxf(m, fmaxf(s_sq[i], s_se[i]));
+  // contributions: thread (part, c) sums the tokens part, part + PARTS, ...
+  const int c = tid % D, part = tid / D;
+  float o = 0.f, l = 0.f;
+#pragma unroll 8
+  for (int i = part; i < n; i += PARTS) {
+    if (s_sq[i] == -INFINITY) continue;
+    const int64_t p = s_idx[i];
+    const float we = fast_exp2(s_se[i] - m), wq = fast_exp2(s_sq[i] - m);
+    const float2 sz = value_sz(g, a.p, blk, p, c);
+    const float vq = sz.y + value_code(g, a.p, blk, p, c, draft) * sz.x;
+    o += we * __half2float(ve[(int64_t)i * D + c]) - wq * vq;
+    l += we - wq;
+  }
+  s_po[part][c] = o;
+  s_pl[part][c] = l;
+  __syncthreads();
   const int row = a.t_exact * a.gs + hl;
-  for (int c = tid; c < D; c += NT) {
-    float o = 0.f, l = 0.f;
-    for (int i = 0; i < n; ++i) {
-      if (s_sq[i] == -INFINITY) continue;
-      const int64_t p = idx[i];
-      const float we = fast_exp2(s_se[i] - m), wq = fast_exp2(s_sq[i] - m);
-      const float2 sz = value_sz(g, a.p, blk, p, c);
-      const float vq = sz.y + value_code(g, a.p, blk, p, c, draft) * sz.x;
-      o += we * __half2float(ve[(int64_t)i * D + c]) - wq * vq;
-      l += we - wq;
+  if (tid < D) {
+    float ot = 0.f, lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < PARTS; ++k) {
+      ot += s_po[k][tid];
+      lt += s_pl[k][tid];
     }
-    po[row * D + c] = o;
-    if (c == 0) {
+    po[row * D + tid] = ot;
+    if (tid == 0) {
       po[RP * D + row] = m;
-      po[RP * D + RP + row] = l;
+      po[RP * D + RP + row] = lt;
     }
   }
 }
