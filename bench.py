@@ -298,6 +298,89 @@ def specache_pipeline(seed, steps=30):
     return res
 
 
+def lwm_128k_steps(seed, steps=64):
+    """The LWM-7B-shaped 128K layer (B=1, Hq=Hkv=32, d=128, G=128, Gv=64,
+    R=256, INT8) as a speculative state machine: from a prefill of
+    L - 4*steps tokens, `steps` steps of {append 6, INT8 verify T=6,
+    rollback 2}, which end at L = 131072 and cross flushes of G=128 tokens
+    (an append that pushes the residual past R quantizes its oldest group);
+    then an INT4 draft at T=1 on the full cache.  K/V are a seeded
+    device draw (only shapes matter for the timing); HIP events around each
+    call."""
+    import torch
+    import kvq_synth as synth
+    import quantized_kv_attention_quant_amd as kq
+    w = synth.WORKLOADS["lwm_7b_128k"]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 13)
+    shape = kq.Shape(B=w.B, Hkv=w.Hkv, d=w.d, G=w.G, Gv=w.Gv, bits=w.bits,
+                     R=w.R, L_max=w.L, max_append=32)
+    cache = kq.QuantKVCache(shape, device=dev)
+    p0 = w.L - 4 * steps
+    K = torch.randn((w.B, p0, w.Hkv, w.d), generator=g, device=dev).half()
+    V = torch.randn((w.B, p0, w.Hkv, w.d), generator=g, device=dev).half()
+    cache.append(K, V)
+    del K, V
+    kn = torch.randn((steps, w.B, 6, w.Hkv, w.d), generator=g, device=dev).half()
+    vn = torch.randn((steps, w.B, 6, w.Hkv, w.d), generator=g, device=dev).half()
+    q6 = torch.from_numpy(synth.queries(w, seed + 5, 6)).to(dev)
+    q1 = torch.from_numpy(synth.queries(w, seed + 6, 1)).to(dev)
+    out6, out1 = torch.empty_like(q6), torch.empty_like(q1)
+    ws = cache.attn_workspace(6, w.Hq)
+    sm = w.d ** -0.5
+    torch.cuda.synchronize()
+    rec = []
+    for i in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        nq0 = cache.n_q
+        e[0].record(stream)
+        kq.kv_quant_append(cache.c, kn[i], vn[i], 6, sh)
+        e[1].record(stream)
+        kq.kv_attn_verify(cache.c, q6, 6, w.Hq, kq.KVQ_TARGET, sm, out6, None,
+                          ws, sh)
+        e[2].record(stream)
+        rec.append((e, cache.n_q > nq0, cache.n_q, cache.n_r))
+        cache.rollback(2)
+    assert cache.n_q + cache.n_r == w.L
+    d1 = []
+    for i in range(20):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        kq.kv_attn_verify(cache.c, q1, 1, w.Hq, kq.KVQ_DRAFT4, sm, out1, None,
+                          ws, sh)
+        e[1].record(stream)
+        d1.append(e)
+    torch.cuda.synchronize()
+    app = [(e[0].elapsed_time(e[1]) * 1e3, fl) for e, fl, _, _ in rec]
+    ver = [e[1].elapsed_time(e[2]) * 1e3 for e, _, _, _ in rec]
+    # the verify's algorithmic bytes at each step's fill level
+    vb = [algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv, nq, nr, 6, 8)
+          for _, _, nq, nr in rec]
+    draft_us = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in d1]))
+    draft_bytes = algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv, cache.n_q,
+                                    cache.n_r, 1, 4)
+    flush = [a for a, fl in app if fl]
+    res = {
+        "workload": "LWM-7B-shaped 128K layer: B=1 Hq=Hkv=32 d=128 "
+                    "L=131072 G=128 Gv=64 R=256 INT8; steps of append 6 / "
+                    "verify T=6 / rollback 2",
+        "steps": steps,
+        "flushes": len(flush),
+        "append6_us": round(float(np.median([a for a, fl in app if not fl])), 3),
+        "append6_flush_us": round(float(np.median(flush)), 3) if flush else None,
+        "verify_int8_t6_us": round(float(np.median(ver)), 3),
+        "verify_int8_t6_gbps": round(float(np.mean(vb)) / (float(np.mean(ver)) * 1e-6) / 1e9, 1),
+        "draft_int4_t1_us": round(draft_us, 3),
+        "draft_int4_t1_gbps": round(draft_bytes / (draft_us * 1e-6) / 1e9, 1),
+    }
+    del cache, kn, vn
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,8 +389,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true",
-                    help="skip the fp16-comparator, gather and prefetch "
-                         "measurements")
+                    help="skip the side measurements (fp16 comparator, "
+                         "gather, prefetch pipeline, 128K layer)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (profiling scale)")
     args = ap.parse_args()
@@ -442,6 +525,7 @@ def main():
         comp["int4_vs_fp16_speedup"] = round(comp["fp16_decode_t1_us"]
                                              / ku["draft_int4_t1"], 3)
         comp["specache_prefetch"] = specache_pipeline(args.seed)
+        comp["lwm_128k"] = lwm_128k_steps(args.seed)
         res["comparators"] = comp
     if args.calibrate_copy:
         calibrate_copy()

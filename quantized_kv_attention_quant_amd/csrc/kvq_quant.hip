@@ -8,12 +8,13 @@
 //
 // One launch covers three kinds of work item (blockIdx.x), each for one
 // (b = blockIdx.z, kvh = blockIdx.y) block:
-//   K-group items: one group of G tokens; thread t owns the channels of
-//     output byte t of a plane row, finds their min/max over the group and
-//     writes codes row by row.
-//   V-tile items:  32 tokens; thread (j, grp) owns the Gv channels of one
-//     token's value group; codes are assembled in LDS into the tiled plane
-//     layout and stored with coalesced dword writes.
+//   K-group items: one group of G tokens; thread (t, qt) owns the channels
+//     of output byte t of a plane row over token slice qt, the slices' min/
+//     max meet in LDS, and each thread writes its slice's codes.
+//   V-tile items:  32 tokens, 8 threads per token over the channels; a
+//     value group's min/max meet by lane shuffles; codes are assembled in
+//     LDS into the tiled plane layout and stored with coalesced dword
+//     writes.
 //   Ring items:    one appended token copied into the fp16 residual ring.
 // The arithmetic is the exact binary32 sequence of the quantizer definition
 // (correctly rounded subtract and divide, round-half-even, RNE to fp16).
@@ -44,33 +45,37 @@ struct Item {
   int k_items, v_items, ring_items;
 };
 
+// Key row of position p: the appended tokens for p >= new0, else the ring
+// slot `slot` (= p mod ring, tracked by the caller: there is no 64-bit
+// divide instruction, and its software sequence per token dominated).
 __device__ inline const __half* key_row(const AppendArgs& a, int b, int kvh,
-                                        int64_t p) {
+                                        int64_t p, int slot) {
   const CacheGeom& g = a.g;
   if (p >= a.new0)
     return a.k_new + (((int64_t)b * a.n + (p - a.new0)) * g.Hkv + kvh) * g.d;
-  int64_t slot = p % g.ring;
-  return a.p.k_res + ((int64_t)b * g.Hkv + kvh) * g.res_block + slot * g.d;
+  return a.p.k_res + ((int64_t)b * g.Hkv + kvh) * g.res_block + (int64_t)slot * g.d;
 }
 
+// Value channel c of position p, given p's ring slot (p mod ring).
 __device__ inline float value_at(const AppendArgs& a, int b, int kvh,
-                                 int64_t p, int c) {
+                                 int64_t p, int slot, int c) {
   const CacheGeom& g = a.g;
   if (p >= a.new0)
     return __half2float(
         a.v_new[(((int64_t)b * a.n + (p - a.new0)) * g.Hkv + kvh) * g.d + c]);
-  int64_t slot = p % g.ring;
   const __half* base = a.p.v_res + ((int64_t)b * g.Hkv + kvh) * g.res_block +
-                       (slot / kTile) * (int64_t)kTile * g.d;
-  return __half2float(base[vres_index((int)(slot % kTile), c, g.d)]);
+                       (int64_t)(slot / kTile) * kTile * g.d;
+  return __half2float(base[vres_index(slot % kTile, c, g.d)]);
 }
 
-// Load `cpt` consecutive halfs (cpt in {2, 4, 8}) as floats.
-__device__ inline void load_chans(const __half* src, int cpt, float* out) {
-  if (cpt == 2) {
+// Load CPT consecutive halfs (CPT in {2, 4, 8}) as floats.
+template <int CPT>
+__device__ inline void load_chans(const __half* src, float* out) {
+  constexpr int cpt = CPT;
+  if constexpr (cpt == 2) {
     __half2 v = *(const __half2*)src;
     out[0] = __low2float(v); out[1] = __high2float(v);
-  } else if (cpt == 4) {
+  } else if constexpr (cpt == 4) {
     uint2 raw = *(const uint2*)src;
     const __half* h = (const __half*)&raw;
 #pragma unroll
@@ -83,56 +88,112 @@ __device__ inline void load_chans(const __half* src, int cpt, float* out) {
   }
 }
 
-__device__ void key_group(const AppendArgs& a, int item, int b, int kvh) {
+// K-group item: threads = output byte column t (the cpt channels of one
+// byte of a plane row) x token slice qt (G / NQ consecutive tokens).  Each
+// thread takes the min/max of its slice, the slices meet in LDS, and each
+// thread then writes the codes of its slice.  A wave's loads cover whole
+// token rows (coalesced) and the token loops are unrolled so several rows
+// are in flight.
+template <int W>   // bits per code in a plane: 4 (8-bit codes), 2, 1
+__device__ void key_group(const AppendArgs& a, int item, int b, int kvh,
+                          float* s_mn, float* s_mx) {
   const CacheGeom& g = a.g;
-  const int cpt = 8 / g.w;          // channels per output byte
-  const int t = threadIdx.x;
-  if (t >= g.d / cpt) return;       // no barriers in this item
-  const int Lv = (1 << g.bits) - 1;
+  constexpr int cpt = 8 / W;                  // channels per output byte
+  constexpr int BITS = W == 4 ? 8 : W;
+  const int cols = g.d / cpt;                 // byte columns (16..64)
+  const int nq = kThreads / cols;             // token slices (4..16)
+  const int tpq = g.G / nq;                   // tokens per slice (>= 2)
+  const int t = threadIdx.x % cols, qt = threadIdx.x / cols;
+  constexpr int Lv = (1 << BITS) - 1;
   const int64_t p0 = a.q0 + (int64_t)item * g.G;
+  const int64_t ps = p0 + (int64_t)qt * tpq;
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
   float mn[8], mx[8], x[8], s[8], z[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) { mn[k] = INFINITY; mx[k] = -INFINITY; }
-  for (int tok = 0; tok < g.G; ++tok) {
-    load_chans(key_row(a, b, kvh, p0 + tok) + t * cpt, cpt, x);
+  const int slot0 = (int)(ps % g.ring);        // ring slot of ps (one divide)
+  auto slot_of = [&](int tok) {                 // (slot0 + tok) mod ring
+    int sl = slot0 + tok;
+    while (sl >= g.ring) sl -= g.ring;
+    return sl;
+  };
+#pragma unroll 8
+  for (int tok = 0; tok < tpq; ++tok) {
+    load_chans<cpt>(key_row(a, b, kvh, ps + tok, slot_of(tok)) + t * cpt, x);
+#pragma unroll
     for (int k = 0; k < cpt; ++k) {
       mn[k] = fminf(mn[k], x[k]);
       mx[k] = fmaxf(mx[k], x[k]);
     }
   }
-  __half2* ksz = a.p.k_sz + blk * g.ksz_block + (p0 / g.G) * g.d + t * cpt;
+#pragma unroll
   for (int k = 0; k < cpt; ++k) {
-    z[k] = mn[k];
-    s[k] = stored_scale(mn[k], mx[k], Lv);
-    ksz[k] = __halves2half2(__float2half_rn(s[k]), __float2half_rn(z[k]));
+    s_mn[qt * g.d + t * cpt + k] = mn[k];
+    s_mx[qt * g.d + t * cpt + k] = mx[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < cpt; ++k) {
+    float lo = INFINITY, hi = -INFINITY;
+    for (int r = 0; r < nq; ++r) {
+      lo = fminf(lo, s_mn[r * g.d + t * cpt + k]);
+      hi = fmaxf(hi, s_mx[r * g.d + t * cpt + k]);
+    }
+    z[k] = lo;
+    s[k] = stored_scale(lo, hi, Lv);
+  }
+  if (qt == 0) {
+    __half2* ksz = a.p.k_sz + blk * g.ksz_block + (p0 / g.G) * g.d + t * cpt;
+#pragma unroll
+    for (int k = 0; k < cpt; ++k)
+      ksz[k] = __halves2half2(__float2half_rn(s[k]), __float2half_rn(z[k]));
   }
   uint8_t* hi = a.p.k_hi + blk * g.k_block_bytes + t;
-  uint8_t* lo = g.bits == 8 ? a.p.k_lo + blk * g.k_block_bytes + t : nullptr;
-  for (int tok = 0; tok < g.G; ++tok) {
-    const int64_t p = p0 + tok;
-    load_chans(key_row(a, b, kvh, p) + t * cpt, cpt, x);
-    unsigned bh = 0, bl = 0;
-    for (int k = 0; k < cpt; ++k) {
-      unsigned q = code_of(x[k], z[k], s[k], Lv);
-      if (g.bits == 8) {
-        bh |= (q >> 4) << (4 * k);
-        bl |= (q & 15u) << (4 * k);
-      } else {
-        bh |= q << (g.w * k);
+  uint8_t* lo = BITS == 8 ? a.p.k_lo + blk * g.k_block_bytes + t : nullptr;
+  // codes in batches of KB tokens: the batch's rows are loaded before its
+  // codes are stored (the compiler cannot reorder a load above a store that
+  // may alias it, so token-by-token the loads would wait in turn)
+  constexpr int KB = 8;
+  for (int t0 = 0; t0 < tpq; t0 += KB) {
+    float xb[KB][8];
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      if (t0 + u < tpq)
+        load_chans<cpt>(key_row(a, b, kvh, ps + t0 + u, slot_of(t0 + u)) + t * cpt,
+                        xb[u]);
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (t0 + u >= tpq) break;
+      const int64_t p = ps + t0 + u;
+      unsigned bh = 0, bl = 0;
+#pragma unroll
+      for (int k = 0; k < cpt; ++k) {
+        unsigned q = code_of(xb[u][k], z[k], s[k], Lv);
+        if constexpr (BITS == 8) {
+          bh |= (q >> 4) << (4 * k);
+          bl |= (q & 15u) << (4 * k);
+        } else {
+          bh |= q << (W * k);
+        }
       }
+      hi[p * g.k_row_bytes] = (uint8_t)bh;
+      if (lo) lo[p * g.k_row_bytes] = (uint8_t)bl;
     }
-    hi[p * g.k_row_bytes] = (uint8_t)bh;
-    if (lo) lo[p * g.k_row_bytes] = (uint8_t)bl;
   }
 }
 
+// V-tile item: 32 tokens, 8 threads per token; thread (j, u) holds the d/8
+// channels u*d/8 .. of token j, a value group spans Gv/(d/8) threads whose
+// min/max meet by lane shuffles.  Codes are assembled in LDS into the tiled
+// plane layout and stored with coalesced dword writes.
 __device__ void value_tile(const AppendArgs& a, int item, int b, int kvh,
                            unsigned* lds_hi, unsigned* lds_lo) {
   const CacheGeom& g = a.g;
   const int Lv = (1 << g.bits) - 1;
   const int ng = g.d / g.Gv;
   const int words = g.d * g.w;             // dwords per plane tile
+  const int cpv = g.d / 8;                 // channels per thread (8 or 16)
+  const int tpg = g.Gv / cpv;              // threads per value group (1..8)
   const int64_t p0 = a.q0 + (int64_t)item * kTile;
   const int64_t tile = p0 / kTile;
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
@@ -141,25 +202,39 @@ __device__ void value_tile(const AppendArgs& a, int item, int b, int kvh,
     lds_lo[i] = 0u;
   }
   __syncthreads();
-  const int j = threadIdx.x % kTile, grp = threadIdx.x / kTile;
-  if (grp < ng) {
-    const int64_t p = p0 + j;
-    float mn = INFINITY, mx = -INFINITY;
-    for (int c = grp * g.Gv; c < (grp + 1) * g.Gv; ++c) {
-      float x = value_at(a, b, kvh, p, c);
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
+  const int j = threadIdx.x / 8, u = threadIdx.x % 8;
+  const int c0 = u * cpv, grp = c0 / g.Gv;
+  const int64_t p = p0 + j;
+  const int slot = (int)(p % g.ring);           // one divide per thread
+  float x[16];
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    if (k < cpv) {
+      x[k] = value_at(a, b, kvh, p, slot, c0 + k);
+      mn = fminf(mn, x[k]);
+      mx = fmaxf(mx, x[k]);
     }
-    const float z = mn, s = stored_scale(mn, mx, Lv);
-    const int gg = (j & 15) >> 2, i = j & 3, h = j >> 4;
+  }
+  for (int o = 1; o < tpg; o <<= 1) {      // lanes of one group: aligned runs
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  const float z = mn, s = stored_scale(mn, mx, Lv);
+  const int gg = (j & 15) >> 2, i = j & 3, h = j >> 4;
+  if (u % tpg == 0) {
     // [part][g][i][group][h]: scale plane then zero-point plane
     __half* sz = (__half*)(a.p.v_sz + blk * g.vsz_block + tile * g.vsz_tile);
     const int at = ((gg * 4 + i) * ng + grp) * 2 + h;
     sz[at] = __float2half_rn(s);
     sz[32 * ng + at] = __float2half_rn(z);
-    const int per = 4 / g.w;
-    for (int c = grp * g.Gv; c < (grp + 1) * g.Gv; ++c) {
-      unsigned q = code_of(value_at(a, b, kvh, p, c), z, s, Lv);
+  }
+  const int per = 4 / g.w;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    if (k < cpv) {
+      const int c = c0 + k;
+      const unsigned q = code_of(x[k], z, s, Lv);
       const int r = c & 15, m = c >> 4;
       const int dw = (16 * gg + r) * (g.d * g.w / 64) + m / per;
       const int bit = 16 * h + g.w * (4 * (m % per) + i);
@@ -204,9 +279,15 @@ __global__ void __launch_bounds__(kThreads)
 append_kernel(AppendArgs a, Item it) {
   __shared__ unsigned lds_hi[128 * 4];
   __shared__ unsigned lds_lo[128 * 4];
+  __shared__ float s_mn[16 * 128], s_mx[16 * 128];   // K slices' min/max
   const int b = blockIdx.z, kvh = blockIdx.y;
   int x = blockIdx.x;
-  if (x < it.k_items) { key_group(a, x, b, kvh); return; }
+  if (x < it.k_items) {
+    if (a.g.w == 4) key_group<4>(a, x, b, kvh, s_mn, s_mx);
+    else if (a.g.w == 2) key_group<2>(a, x, b, kvh, s_mn, s_mx);
+    else key_group<1>(a, x, b, kvh, s_mn, s_mx);
+    return;
+  }
   x -= it.k_items;
   if (x < it.v_items) { value_tile(a, x, b, kvh, lds_hi, lds_lo); return; }
   x -= it.v_items;
