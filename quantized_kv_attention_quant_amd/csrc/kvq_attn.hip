@@ -1290,13 +1290,14 @@ hipError_t by_rows(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 // Splits per block: enough workgroups to fill every resident slot once,
-// choosing among 1x..4x the minimum the count whose last dispatch wave is
-// fullest; no more than one split per `streams` units and no more than cap.
+// choosing among 1x..8x the minimum (up to cap) the count whose last
+// dispatch wave is fullest (the smallest such count on ties); no more than
+// one split per `streams` units.
 int plan_splits(int64_t nb, int64_t slots, int64_t units, int streams, int cap) {
   const int64_t smin = cdiv(slots, nb);
   int64_t best = smin;
   double best_eff = -1.0;
-  for (int64_t s = smin; s <= 4 * smin; ++s) {
+  for (int64_t s = smin; s <= 8 * smin && s <= cap; ++s) {
     const int64_t wg = nb * s;
     const double eff = (double)wg / (double)(slots * cdiv(wg, slots));
     if (eff > best_eff + 1e-9) {
