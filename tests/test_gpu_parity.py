@@ -29,6 +29,10 @@ SMALL = {
     "gqa_1bit": W("gqa_1bit", 2, 8, 2, 128, 1000, 32, 32, 32, 1, "normal"),
     "d64_2bit": W("d64_2bit", 1, 4, 2, 64, 500, 32, 16, 64, 2, "normal"),
     "gv128": W("gv128", 1, 4, 1, 128, 700, 64, 128, 64, 8, "outlier"),
+    # key groups of 96 tokens: not a power of two, and groups straddle the
+    # top-k's 1024-token chunks
+    "g96": W("g96", 1, 8, 2, 128, 2400, 96, 64, 192, 8, "outlier"),
+    "g96_2bit": W("g96_2bit", 1, 8, 2, 128, 2000, 96, 32, 96, 2, "normal"),
 }
 
 
@@ -72,7 +76,7 @@ def test_append_bulk_bit_exact(name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "gqa_d128_int8", "gqa_2bit",
-                                  "gqa_1bit", "mha_d64_int8"])
+                                  "gqa_1bit", "mha_d64_int8", "g96"])
 def test_append_incremental_and_rollback(name):
     w = SMALL[name]
     say(f"[gpu] append incremental {name}")
@@ -105,7 +109,8 @@ RUNS = [("tiny", "target", 1), ("tiny", "draft4", 1), ("tiny", "target", 8),
         ("mha_d64_int8", "target", 9), ("mha_d64_int8", "draft4", 3),
         ("gqa_2bit", "target", 2), ("gqa_2bit", "target", 8),
         ("gqa_1bit", "target", 2), ("d64_2bit", "target", 5),
-        ("gv128", "target", 4), ("gv128", "draft4", 8)]
+        ("gv128", "target", 4), ("gv128", "draft4", 8),
+        ("g96", "target", 7), ("g96", "draft4", 1), ("g96_2bit", "target", 2)]
 
 
 @pytest.mark.parametrize("name,path,T", RUNS)
@@ -176,7 +181,8 @@ def test_verify_row_equals_prefix_decode():
 @pytest.mark.parametrize("name,path,k", [
     ("gqa_d128_int8", "target", 64), ("gqa_d128_int8", "draft4", 64),
     ("gqa_2bit", "target", 64), ("gqa_1bit", "target", 100),
-    ("mha_d64_int8", "target", 256), ("tiny", "target", 300 // 2)])
+    ("mha_d64_int8", "target", 256), ("tiny", "target", 300 // 2),
+    ("g96", "target", 64), ("g96", "draft4", 64), ("g96_2bit", "target", 200)])
 def test_topk_bit_exact(name, path, k):
     w = SMALL[name]
     say(f"[gpu] topk {name} {path} k={k}")
