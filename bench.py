@@ -381,6 +381,71 @@ def lwm_128k_steps(seed, steps=64):
     return res
 
 
+def llama2_8k(seed, steps=50):
+    """The Llama-2-7B-shaped 8K layer (B=1, Hq=Hkv=32, d=128, G=128, Gv=64,
+    R=256, INT8): INT8 verify at T=9 and INT4 draft at T=1, each call on one
+    of 4 cache copies (4 x 72 MB, more than the Infinity Cache) appended
+    with the T query tokens and rolled back after.  K/V are a seeded device
+    draw; HIP events around each attention call."""
+    import torch
+    import kvq_synth as synth
+    import quantized_kv_attention_quant_amd as kq
+    w = synth.WORKLOADS["llama2_7b_8k"]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 17)
+    T = 9
+    shape = kq.Shape(B=w.B, Hkv=w.Hkv, d=w.d, G=w.G, Gv=w.Gv, bits=w.bits,
+                     R=w.R, L_max=w.L, max_append=32)
+    base = kq.QuantKVCache(shape, device=dev)
+    K = torch.randn((w.B, w.L - T, w.Hkv, w.d), generator=g, device=dev).half()
+    V = torch.randn((w.B, w.L - T, w.Hkv, w.d), generator=g, device=dev).half()
+    base.append(K, V)
+    del K, V
+    caches = [base] + [base.clone() for _ in range(3)]
+    kn = torch.randn((w.B, T, w.Hkv, w.d), generator=g, device=dev).half()
+    vn = torch.randn((w.B, T, w.Hkv, w.d), generator=g, device=dev).half()
+    q9 = torch.from_numpy(synth.queries(w, seed + 7, T)).to(dev)
+    q1 = torch.from_numpy(synth.queries(w, seed + 8, 1)).to(dev)
+    out9, out1 = torch.empty_like(q9), torch.empty_like(q1)
+    ws = base.attn_workspace(T, w.Hq)
+    sm = w.d ** -0.5
+
+    def run(path, TT, q, out):
+        ts = []
+        for i in range(steps + 5):
+            c = caches[i % 4]
+            kq.kv_quant_append(c.c, kn, vn, T, sh)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            kq.kv_attn_verify(c.c, q, TT, w.Hq, path, sm, out, None, ws, sh)
+            e1.record(stream)
+            kq.kv_rollback(c.c, T)
+            if i >= 5:
+                ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
+
+    v_us = run(kq.KVQ_TARGET, T, q9, out9)
+    d_us = run(kq.KVQ_DRAFT4, 1, q1, out1)
+    n_q, n_r = base.n_q, base.n_r + T
+    vb = algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv, n_q, n_r, T, 8)
+    db = algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv, n_q, n_r, 1, 4)
+    del caches, base
+    torch.cuda.empty_cache()
+    return {
+        "workload": "Llama-2-7B-shaped 8K layer: B=1 Hq=Hkv=32 d=128 L=8192 "
+                    "G=128 Gv=64 R=256 INT8",
+        "verify_int8_t9_us": round(v_us, 3),
+        "verify_int8_t9_gbps": round(vb / (v_us * 1e-6) / 1e9, 1),
+        "draft_int4_t1_us": round(d_us, 3),
+        "draft_int4_t1_gbps": round(db / (d_us * 1e-6) / 1e9, 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,7 +455,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true",
                     help="skip the side measurements (fp16 comparator, "
-                         "gather, prefetch pipeline, 128K layer)")
+                         "gather, prefetch pipeline, 128K and 8K layers)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (profiling scale)")
     args = ap.parse_args()
@@ -526,6 +591,7 @@ def main():
                                              / ku["draft_int4_t1"], 3)
         comp["specache_prefetch"] = specache_pipeline(args.seed)
         comp["lwm_128k"] = lwm_128k_steps(args.seed)
+        comp["llama2_8k"] = llama2_8k(args.seed)
         res["comparators"] = comp
     if args.calibrate_copy:
         calibrate_copy()
