@@ -374,123 +374,165 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
     a.lse[((int64_t)b * a.Hq + h) * a.T + t] = (M + __log2f(lsum)) * kLn2;
 }
 
-// Exact substitution, one workgroup per (GQA head hl, kv head, batch): the
-// partial that turns query row t_exact * gs + hl's attention over the
-// quantized cache into attention where the positions idx_exact read the
-// exact fp16 K/V (SpeCache page, Approach: the fetched pairs are used in
-// full precision for the output token).  With logits in the log2 domain,
-// sq_j from the dequantized key and se_j from the exact one:
+// Exact substitution, one workgroup per (group of up to HB GQA heads, kv
+// head, batch): the partial that turns query row t_exact * gs + hl's
+// attention over the quantized cache into attention where the positions
+// idx_exact read the exact fp16 K/V (SpeCache page, Approach: the fetched
+// pairs are used in full precision for the output token).  With logits in
+// the log2 domain, sq_j from the dequantized key and se_j from the exact one:
 //   l = sum_j (2^(se_j - m) - 2^(sq_j - m)),
 //   o = sum_j (2^(se_j - m) v_j - 2^(sq_j - m) v^_j),   m = max_j (sq_j, se_j)
 // written to the spare partial slot S of the block; the log-sum-exp merge of
 // the S + 1 partials then removes each fetched token's quantized term and
-// adds its exact one.  The other query rows of head hl get an empty partial
-// (m = -inf, l = 0, o = 0).  Positions outside [0, n_q) are skipped.
-// A wave scores fetched tokens with its lanes over the channels, four
-// tokens in flight at a time; the output pass runs threads over (token
-// subset, channel) so the code and scale loads of many tokens are in flight
-// together, and the subsets meet in LDS.
+// adds its exact one.  The other query rows of those heads get an empty
+// partial (m = -inf, l = 0, o = 0).  Positions outside [0, n_q) are skipped.
+// Each fetched token's quantized and exact K/V are loaded once for the
+// workgroup's heads (the heads of a kv group read the same rows).  1024
+// threads: a wave scores tokens with its lanes over the channels, two
+// tokens in flight (32 tokens per round over the 16 waves); the output
+// pass runs threads over (token subset, channel), 8 subsets at d = 128, and
+// the subsets meet in LDS.  Both passes are branch-free over skipped entries (stand-in
+// position 0, terms selected away), so the loads of many tokens issue
+// together.
 template <int D, int RP>
-__global__ void __launch_bounds__(256) exact_kernel(const AttnArgs a) {
-  constexpr int NT = 256;
+__global__ void __launch_bounds__(1024) exact_kernel(const AttnArgs a) {
+  constexpr int NT = 1024, HB = 4;               // heads per workgroup
   constexpr int PARTS = NT / D;                  // token subsets in the output pass
-  __shared__ float s_q[D];
-  __shared__ float s_sq[kMaxExact], s_se[kMaxExact];
+  __shared__ float s_q[HB][D];
+  __shared__ float s_sq[HB][kMaxExact], s_se[HB][kMaxExact];
   __shared__ int s_idx[kMaxExact];
-  __shared__ float s_po[PARTS][D], s_pl[PARTS][D];
+  __shared__ float s_po[PARTS][HB][D], s_pl[PARTS][HB], s_m[HB];
   const CacheGeom& g = a.g;
-  const int hl = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int hl0 = blockIdx.x * HB, kvh = blockIdx.y, b = blockIdx.z;
+  const int nh = a.gs - hl0 < HB ? a.gs - hl0 : HB;   // heads of this workgroup
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
   const int tid = threadIdx.x;
-  const int n = a.n_exact, h = kvh * a.gs + hl;
+  const int n = a.n_exact;
   const bool draft = a.path == KVQ_DRAFT4;
   const int64_t pstride = (int64_t)RP * (D + 2);
   float* po = a.ws + (blk * a.s_alloc + a.S) * pstride;
   const __half* ke = a.k_exact + blk * n * D;
   const __half* ve = a.v_exact + blk * n * D;
 
-  // empty partial for this head's other query rows
+  // empty partials for these heads' other query rows
   for (int t = 0; t < a.T; ++t) {
     if (t == a.t_exact) continue;
-    const int r = t * a.gs + hl;
-    for (int c = tid; c < D; c += NT) po[r * D + c] = 0.f;
-    if (tid == 0) {
-      po[RP * D + r] = -INFINITY;
-      po[RP * D + RP + r] = 0.f;
+    for (int hh = 0; hh < nh; ++hh) {
+      const int r = t * a.gs + hl0 + hh;
+      for (int c = tid; c < D; c += NT) po[r * D + c] = 0.f;
+      if (tid == 0) {
+        po[RP * D + r] = -INFINITY;
+        po[RP * D + RP + r] = 0.f;
+      }
     }
   }
-  if (tid < D)
-    s_q[tid] = __half2float(a.q[(((int64_t)b * a.T + a.t_exact) * a.Hq + h) * D + tid]);
+  for (int e = tid; e < HB * D; e += NT) {
+    const int hh = e / D, c = e % D;
+    s_q[hh][c] = hh < nh ? __half2float(a.q[(((int64_t)b * a.T + a.t_exact) * a.Hq +
+                                             kvh * a.gs + hl0 + hh) * D + c])
+                         : 0.f;
+  }
   for (int i = tid; i < n; i += NT) s_idx[i] = a.idx_exact[blk * n + i];
   __syncthreads();
 
-  // logits of the dequantized and the exact key: one wave per token, lanes
-  // over channels (coalesced), UT tokens of a wave in flight together
-  constexpr int NWV = NT / kWave, UT = 4;
+  // logits of the dequantized and the exact key, for every head
+  constexpr int NWV = NT / kWave, UT = 2;
   const int wave = tid / kWave, lane = tid % kWave;
   for (int i0 = wave; i0 < n; i0 += NWV * UT) {
-    float dq[UT], de[UT];
+    float dq[UT][HB], de[UT][HB];
     bool ok[UT];
 #pragma unroll
     for (int u = 0; u < UT; ++u) {
       const int i = i0 + u * NWV;
       const int64_t p = i < n ? s_idx[i] : -1;
       ok[u] = p >= 0 && p < a.n_q;
-      dq[u] = de[u] = 0.f;
-      if (ok[u]) {
+      const int64_t ps = ok[u] ? p : 0;        // stand-in: discarded below
+      const int64_t is = i < n ? i : 0;
 #pragma unroll
-        for (int c = lane; c < D; c += kWave) {
-          const __half2 sz = key_sz(g, a.p, blk, p, c);
-          const float kq = __high2float(sz) + key_code(g, a.p, blk, p, c, draft) * __low2float(sz);
-          dq[u] += s_q[c] * kq;
-          de[u] += s_q[c] * __half2float(ke[(int64_t)i * D + c]);
+      for (int hh = 0; hh < HB; ++hh) dq[u][hh] = de[u][hh] = 0.f;
+#pragma unroll
+      for (int c = lane; c < D; c += kWave) {
+        const __half2 sz = key_sz(g, a.p, blk, ps, c);
+        const float kq = __high2float(sz) + key_code(g, a.p, blk, ps, c, draft) * __low2float(sz);
+        const float kx = __half2float(ke[is * D + c]);
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) {
+          dq[u][hh] += s_q[hh][c] * kq;
+          de[u][hh] += s_q[hh][c] * kx;
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < UT; ++u) {
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        dq[u] += __shfl_xor(dq[u], o);
-        de[u] += __shfl_xor(de[u], o);
-      }
+      for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          dq[u][hh] += __shfl_xor(dq[u][hh], o);
+          de[u][hh] += __shfl_xor(de[u][hh], o);
+        }
       const int i = i0 + u * NWV;
-      if (lane == 0 && i < n) {
-        s_sq[i] = ok[u] ? dq[u] * a.c0 : -INFINITY;
-        s_se[i] = ok[u] ? de[u] * a.c0 : -INFINITY;
+      if (lane < HB && i < n) {
+        float q = dq[u][0], e = de[u][0];
+#pragma unroll
+        for (int hh = 1; hh < HB; ++hh)
+          if (lane == hh) { q = dq[u][hh]; e = de[u][hh]; }
+        s_sq[lane][i] = ok[u] ? q * a.c0 : -INFINITY;
+        s_se[lane][i] = ok[u] ? e * a.c0 : -INFINITY;
       }
     }
   }
   __syncthreads();
-  float m = -INFINITY;
-  for (int i = 0; i < n; ++i) m = fmaxf(m, fmaxf(s_sq[i], s_se[i]));
+  // per-head reference m = max over the tokens of both logits: wave hh
+  if (wave < HB) {
+    float mx = -INFINITY;
+    for (int i = lane; i < n; i += kWave)
+      mx = fmaxf(mx, fmaxf(s_sq[wave][i], s_se[wave][i]));
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) s_m[wave] = mx;
+  }
+  __syncthreads();
+  float m[HB];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) m[hh] = s_m[hh];
   // contributions: thread (part, c) sums the tokens part, part + PARTS, ...
   const int c = tid % D, part = tid / D;
-  float o = 0.f, l = 0.f;
-#pragma unroll 8
+  float o[HB], l[HB];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) o[hh] = l[hh] = 0.f;
+#pragma unroll 4
   for (int i = part; i < n; i += PARTS) {
-    if (s_sq[i] == -INFINITY) continue;
-    const int64_t p = s_idx[i];
-    const float we = fast_exp2(s_se[i] - m), wq = fast_exp2(s_sq[i] - m);
+    const bool ok = s_sq[0][i] != -INFINITY;   // validity is per token
+    const int64_t p = ok ? s_idx[i] : 0;
     const float2 sz = value_sz(g, a.p, blk, p, c);
     const float vq = sz.y + value_code(g, a.p, blk, p, c, draft) * sz.x;
-    o += we * __half2float(ve[(int64_t)i * D + c]) - wq * vq;
-    l += we - wq;
+    const float vx = __half2float(ve[(int64_t)i * D + c]);
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      const float we = fast_exp2(s_se[hh][i] - m[hh]), wq = fast_exp2(s_sq[hh][i] - m[hh]);
+      o[hh] += ok ? we * vx - wq * vq : 0.f;   // selected: stand-ins never enter
+      l[hh] += ok ? we - wq : 0.f;
+    }
   }
-  s_po[part][c] = o;
-  s_pl[part][c] = l;
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    s_po[part][hh][c] = o[hh];
+    if (c == 0) s_pl[part][hh] = l[hh];
+  }
   __syncthreads();
-  const int row = a.t_exact * a.gs + hl;
-  if (tid < D) {
+  for (int e = tid; e < nh * D; e += NT) {
+    const int hh = e / D, cc = e % D;
     float ot = 0.f, lt = 0.f;
 #pragma unroll
     for (int k = 0; k < PARTS; ++k) {
-      ot += s_po[k][tid];
-      lt += s_pl[k][tid];
+      ot += s_po[k][hh][cc];
+      lt += s_pl[k][hh];
     }
-    po[row * D + tid] = ot;
-    if (tid == 0) {
-      po[RP * D + row] = m;
+    const int row = a.t_exact * a.gs + hl0 + hh;
+    po[row * D + cc] = ot;
+    if (cc == 0) {
+      po[RP * D + row] = m[hh];
       po[RP * D + RP + row] = lt;
     }
   }
@@ -1257,8 +1299,8 @@ hipError_t go(AttnArgs a, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (a.n_exact >= 0) {
     hipLaunchKernelGGL((exact_kernel<D, C::RP>),
-                       dim3((unsigned)a.gs, (unsigned)a.g.Hkv, (unsigned)a.g.B),
-                       dim3(256), 0, s, a);
+                       dim3((unsigned)cdiv(a.gs, 4), (unsigned)a.g.Hkv, (unsigned)a.g.B),
+                       dim3(1024), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     ++a.S;                       // the merge reads the substitution partial too

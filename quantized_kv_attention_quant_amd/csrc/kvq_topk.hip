@@ -22,7 +22,8 @@
 //     same thread or wave are exchanged by lane shuffles, and only the 3
 //     stages whose partners sit in another wave go through LDS.  The
 //     chunk's best k go to the workspace.
-//   merge_kernel, grid Hkv x B: sorts a block's chunk candidates in LDS and
+//   merge_kernel, grid Hkv x B, 512 threads: sorts a block's chunk
+//     candidates with the same register network, 2048 at a time, and
 //     writes the best k.  The kernel boundary makes the candidates visible;
 //     no fence or counter is needed.
 #include "kvq_internal.h"
@@ -49,26 +50,6 @@ __device__ __forceinline__ float key_of(unsigned long long c) {
   return __uint_as_float(u);
 }
 
-// Descending bitonic sort of n (power of two) composites in LDS.
-__device__ void sort_desc(unsigned long long* v, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += NT) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long x = v[i], y = v[ixj];
-          const bool up = (i & k) == 0;   // this run ends descending
-          if (up ? (x < y) : (x > y)) {
-            v[i] = y;
-            v[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x,
                                                          int m) {
   const unsigned lo = __shfl_xor((unsigned)x, m);
@@ -76,14 +57,15 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x,
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Descending bitonic sort of the workgroup's NT * 4 composites, element
+// Descending bitonic sort of the workgroup's NTS * 4 composites, element
 // 4 * tid + m in e[m].  Element i meets i ^ j at stage (k, j); the pair is
-// put in descending order when (i & k) == 0, ascending otherwise (the same
-// network as sort_desc).
+// put in descending order when (i & k) == 0, ascending otherwise, so the
+// run of every stage k ends ordered and the last one sorts all elements.
+template <int NTS>
 __device__ void sort_regs_desc(unsigned long long (&e)[TPT],
                                unsigned long long* lds) {
   const int tid = threadIdx.x;
-  for (int k = 2; k <= NT * TPT; k <<= 1) {
+  for (int k = 2; k <= NTS * TPT; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       if (j < TPT) {                      // both elements in this thread
 #pragma unroll
@@ -235,42 +217,53 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
     comp[m] = cm;
   }
 
-  sort_regs_desc(comp, s_x);
+  sort_regs_desc<NT>(comp, s_x);
   unsigned long long* cand = a.cand + (blk * a.chunks + chunk) * a.k;
 #pragma unroll
   for (int m = 0; m < TPT; ++m)
     if (TPT * tid + m < a.k) cand[TPT * tid + m] = comp[m];
 }
 
-// One workgroup per block: the best k of the chunks' candidates.
-__global__ void __launch_bounds__(NT) merge_kernel(const TopkArgs a) {
-  __shared__ unsigned long long s_c[2 * kChunk];
+// One workgroup per block: the best k of the chunks' candidates, sorted in
+// registers 2048 at a time (the best k stay in place, the rest refill).
+constexpr int NTM = 512;                 // merge threads
+__global__ void __launch_bounds__(NTM) merge_kernel(const TopkArgs a) {
+  __shared__ unsigned long long s_x[NTM * TPT];
+  constexpr int cap = NTM * TPT;
   const int b = blockIdx.y, kvh = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t blk = (int64_t)b * a.g.Hkv + kvh;
-  // keep the best k in s_c[0, k); refill the rest in batches
   const unsigned long long* all = a.cand + blk * a.chunks * a.k;
   const int total = a.chunks * a.k;
-  const int cap = 2 * kChunk;
-  for (int i = tid; i < cap; i += NT) s_c[i] = i < total ? all[i] : 0ull;
-  int taken = total < cap ? total : cap;
-  __syncthreads();
-  sort_desc(s_c, cap);
-  while (taken < total) {
-    const int room = cap - a.k;
-    for (int i = tid; i < room; i += NT)
-      s_c[a.k + i] = taken + i < total ? all[taken + i] : 0ull;
-    taken += room;
-    __syncthreads();
-    sort_desc(s_c, cap);
+  unsigned long long e[TPT];
+#pragma unroll
+  for (int m = 0; m < TPT; ++m) {
+    const int i = TPT * tid + m;
+    e[m] = i < total ? all[i] : 0ull;
+  }
+  sort_regs_desc<NTM>(e, s_x);
+  for (int taken = cap; taken < total; taken += cap - a.k) {
+#pragma unroll
+    for (int m = 0; m < TPT; ++m) {
+      const int i = TPT * tid + m;
+      if (i >= a.k) {
+        const int src = taken + i - a.k;
+        e[m] = src < total ? all[src] : 0ull;
+      }
+    }
+    sort_regs_desc<NTM>(e, s_x);
   }
   int32_t* idx = a.idx + blk * a.k;
   float* key = a.key ? a.key + blk * a.k : nullptr;
-  for (int i = tid; i < a.k; i += NT) {
-    const unsigned long long c = s_c[i];
-    const bool valid = c != 0ull;
-    idx[i] = valid ? (int32_t)(0xFFFFFFFFu - (unsigned)(c & 0xFFFFFFFFu)) : -1;
-    if (key) key[i] = valid ? key_of(c) : -INFINITY;
+#pragma unroll
+  for (int m = 0; m < TPT; ++m) {
+    const int i = TPT * tid + m;
+    if (i < a.k) {
+      const unsigned long long c = e[m];
+      const bool valid = c != 0ull;
+      idx[i] = valid ? (int32_t)(0xFFFFFFFFu - (unsigned)(c & 0xFFFFFFFFu)) : -1;
+      if (key) key[i] = valid ? key_of(c) : -INFINITY;
+    }
   }
 }
 
@@ -280,7 +273,7 @@ hipError_t go(const TopkArgs& a, hipStream_t s) {
                      dim3(a.chunks, a.g.Hkv, a.g.B), dim3(NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.g.Hkv, a.g.B), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel, dim3(a.g.Hkv, a.g.B), dim3(NTM), 0, s, a);
   return hipGetLastError();
 }
 
