@@ -386,27 +386,26 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
 // the S + 1 partials then removes each fetched token's quantized term and
 // adds its exact one.  The other query rows of those heads get an empty
 // partial (m = -inf, l = 0, o = 0).  Positions outside [0, n_q) are skipped.
-// Each fetched token's quantized and exact K/V are loaded once for the
-// workgroup's heads (the heads of a kv group read the same rows).  1024
-// threads: a wave scores tokens with its lanes over the channels, two
-// tokens in flight (32 tokens per round over the 16 waves); the output
-// pass runs threads over (token subset, channel), 8 subsets at d = 128, and
-// the subsets meet in LDS.  Both passes are branch-free over skipped entries (stand-in
-// position 0, terms selected away), so the loads of many tokens issue
-// together.
+// 1024 threads: each wave takes fetched tokens w, w + 16, ... with its lanes
+// over the channels and issues all K and V loads of UT tokens together (the
+// positions are scattered, so each round of loads is long); the heads of
+// the kv group share the loaded rows.  Each wave keeps (m, l, o) per head
+// with the usual rescaling, and the 16 wave states meet in LDS by
+// log-sum-exp.  Skipped entries read stand-in position 0 and are never
+// folded in.
 template <int D, int RP>
 __global__ void __launch_bounds__(1024) exact_kernel(const AttnArgs a) {
   constexpr int NT = 1024, HB = 4;               // heads per workgroup
-  constexpr int PARTS = NT / D;                  // token subsets in the output pass
+  constexpr int NWV = NT / kWave, CPL = D / kWave;
+  constexpr int UT = CPL == 1 ? 4 : 2;          // tokens a wave loads together
   __shared__ float s_q[HB][D];
-  __shared__ float s_sq[HB][kMaxExact], s_se[HB][kMaxExact];
   __shared__ int s_idx[kMaxExact];
-  __shared__ float s_po[PARTS][HB][D], s_pl[PARTS][HB], s_m[HB];
+  __shared__ float s_o[NWV][HB][D], s_m[NWV][HB], s_l[NWV][HB];
   const CacheGeom& g = a.g;
   const int hl0 = blockIdx.x * HB, kvh = blockIdx.y, b = blockIdx.z;
   const int nh = a.gs - hl0 < HB ? a.gs - hl0 : HB;   // heads of this workgroup
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = a.n_exact;
   const bool draft = a.path == KVQ_DRAFT4;
   const int64_t pstride = (int64_t)RP * (D + 2);
@@ -435,104 +434,96 @@ __global__ void __launch_bounds__(1024) exact_kernel(const AttnArgs a) {
   for (int i = tid; i < n; i += NT) s_idx[i] = a.idx_exact[blk * n + i];
   __syncthreads();
 
-  // logits of the dequantized and the exact key, for every head
-  constexpr int NWV = NT / kWave, UT = 2;
-  const int wave = tid / kWave, lane = tid % kWave;
+  float m[HB], l[HB], o[HB][CPL];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) o[hh][k] = 0.f;
+  }
   for (int i0 = wave; i0 < n; i0 += NWV * UT) {
-    float dq[UT][HB], de[UT][HB];
+    // every load of the UT tokens first
+    float kq[UT][CPL], kx[UT][CPL], vq[UT][CPL], vx[UT][CPL];
     bool ok[UT];
 #pragma unroll
     for (int u = 0; u < UT; ++u) {
       const int i = i0 + u * NWV;
       const int64_t p = i < n ? s_idx[i] : -1;
       ok[u] = p >= 0 && p < a.n_q;
-      const int64_t ps = ok[u] ? p : 0;        // stand-in: discarded below
+      const int64_t ps = ok[u] ? p : 0;        // stand-in: never folded in
       const int64_t is = i < n ? i : 0;
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh) dq[u][hh] = de[u][hh] = 0.f;
-#pragma unroll
-      for (int c = lane; c < D; c += kWave) {
+      for (int k = 0; k < CPL; ++k) {
+        const int c = lane + kWave * k;
         const __half2 sz = key_sz(g, a.p, blk, ps, c);
-        const float kq = __high2float(sz) + key_code(g, a.p, blk, ps, c, draft) * __low2float(sz);
-        const float kx = __half2float(ke[is * D + c]);
-#pragma unroll
-        for (int hh = 0; hh < HB; ++hh) {
-          dq[u][hh] += s_q[hh][c] * kq;
-          de[u][hh] += s_q[hh][c] * kx;
-        }
+        kq[u][k] = __high2float(sz) + key_code(g, a.p, blk, ps, c, draft) * __low2float(sz);
+        kx[u][k] = __half2float(ke[is * D + c]);
+        const float2 vs = value_sz(g, a.p, blk, ps, c);
+        vq[u][k] = vs.y + value_code(g, a.p, blk, ps, c, draft) * vs.x;
+        vx[u][k] = __half2float(ve[is * D + c]);
       }
     }
 #pragma unroll
     for (int u = 0; u < UT; ++u) {
+      float dq[HB], de[HB];
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh)
+      for (int hh = 0; hh < HB; ++hh) {
+        dq[hh] = de[hh] = 0.f;
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          dq[u][hh] += __shfl_xor(dq[u][hh], o);
-          de[u][hh] += __shfl_xor(de[u][hh], o);
+        for (int k = 0; k < CPL; ++k) {
+          dq[hh] += s_q[hh][lane + kWave * k] * kq[u][k];
+          de[hh] += s_q[hh][lane + kWave * k] * kx[u][k];
         }
-      const int i = i0 + u * NWV;
-      if (lane < HB && i < n) {
-        float q = dq[u][0], e = de[u][0];
 #pragma unroll
-        for (int hh = 1; hh < HB; ++hh)
-          if (lane == hh) { q = dq[u][hh]; e = de[u][hh]; }
-        s_sq[lane][i] = ok[u] ? q * a.c0 : -INFINITY;
-        s_se[lane][i] = ok[u] ? e * a.c0 : -INFINITY;
+        for (int sh = 1; sh < kWave; sh <<= 1) {
+          dq[hh] += __shfl_xor(dq[hh], sh);
+          de[hh] += __shfl_xor(de[hh], sh);
+        }
       }
-    }
-  }
-  __syncthreads();
-  // per-head reference m = max over the tokens of both logits: wave hh
-  if (wave < HB) {
-    float mx = -INFINITY;
-    for (int i = lane; i < n; i += kWave)
-      mx = fmaxf(mx, fmaxf(s_sq[wave][i], s_se[wave][i]));
+      if (ok[u]) {                              // wave-uniform: one token per wave
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if (lane == 0) s_m[wave] = mx;
-  }
-  __syncthreads();
-  float m[HB];
+        for (int hh = 0; hh < HB; ++hh) {
+          const float sq = dq[hh] * a.c0, se = de[hh] * a.c0;
+          const float mn = fmaxf(m[hh], fmaxf(sq, se));
+          const float alpha = fast_exp2(m[hh] - mn);   // 0 while m = -inf
+          const float we = fast_exp2(se - mn), wq = fast_exp2(sq - mn);
+          l[hh] = l[hh] * alpha + (we - wq);
 #pragma unroll
-  for (int hh = 0; hh < HB; ++hh) m[hh] = s_m[hh];
-  // contributions: thread (part, c) sums the tokens part, part + PARTS, ...
-  const int c = tid % D, part = tid / D;
-  float o[HB], l[HB];
-#pragma unroll
-  for (int hh = 0; hh < HB; ++hh) o[hh] = l[hh] = 0.f;
-#pragma unroll 4
-  for (int i = part; i < n; i += PARTS) {
-    const bool ok = s_sq[0][i] != -INFINITY;   // validity is per token
-    const int64_t p = ok ? s_idx[i] : 0;
-    const float2 sz = value_sz(g, a.p, blk, p, c);
-    const float vq = sz.y + value_code(g, a.p, blk, p, c, draft) * sz.x;
-    const float vx = __half2float(ve[(int64_t)i * D + c]);
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      const float we = fast_exp2(s_se[hh][i] - m[hh]), wq = fast_exp2(s_sq[hh][i] - m[hh]);
-      o[hh] += ok ? we * vx - wq * vq : 0.f;   // selected: stand-ins never enter
-      l[hh] += ok ? we - wq : 0.f;
+          for (int k = 0; k < CPL; ++k)
+            o[hh][k] = o[hh][k] * alpha + (we * vx[u][k] - wq * vq[u][k]);
+          m[hh] = mn;
+        }
+      }
     }
   }
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
-    s_po[part][hh][c] = o[hh];
-    if (c == 0) s_pl[part][hh] = l[hh];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) s_o[wave][hh][lane + kWave * k] = o[hh][k];
+    if (lane == 0) {
+      s_m[wave][hh] = m[hh];
+      s_l[wave][hh] = l[hh];
+    }
   }
   __syncthreads();
   for (int e = tid; e < nh * D; e += NT) {
-    const int hh = e / D, cc = e % D;
+    const int hh = e / D, c = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, s_m[w][hh]);
     float ot = 0.f, lt = 0.f;
 #pragma unroll
-    for (int k = 0; k < PARTS; ++k) {
-      ot += s_po[k][hh][cc];
-      lt += s_pl[k][hh];
+    for (int w = 0; w < NWV; ++w) {
+      const float mw = s_m[w][hh];
+      const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+      ot += s_o[w][hh][c] * sc;
+      lt += s_l[w][hh] * sc;
     }
     const int row = a.t_exact * a.gs + hl0 + hh;
-    po[row * D + cc] = ot;
-    if (cc == 0) {
-      po[RP * D + row] = m[hh];
+    po[row * D + c] = ot;
+    if (c == 0) {
+      po[RP * D + row] = M;
       po[RP * D + RP + row] = lt;
     }
   }
