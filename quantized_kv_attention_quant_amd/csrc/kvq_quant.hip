@@ -8,9 +8,9 @@
 //
 // One launch covers three kinds of work item (blockIdx.x), each for one
 // (b = blockIdx.z, kvh = blockIdx.y) block:
-//   K-group items: one group of G tokens; thread (t, qt) owns the channels
-//     of output byte t of a plane row over token slice qt, the slices' min/
-//     max meet in LDS, and each thread writes its slice's codes.
+//   K-group items: one group of G tokens; thread (t, qt) owns 8 channels
+//     over token slice qt, the slices' min/max meet in LDS, and each thread
+//     writes its slice's codes as whole words of the plane rows.
 //   V-tile items:  32 tokens, 8 threads per token over the channels; a
 //     value group's min/max meet by lane shuffles; codes are assembled in
 //     LDS into the tiled plane layout and stored with coalesced dword
@@ -41,8 +41,14 @@ __device__ inline unsigned code_of(float x, float z, float s, int Lv) {
   return (unsigned)r;
 }
 
+// Work items of one launch.  Bulk appends give each V-tile workgroup vt
+// tiles and each ring workgroup rt tokens (fewer, larger workgroups: a
+// 32K-token prefill would otherwise dispatch ~100K tiny ones); a per-step
+// append keeps one tile and one token per workgroup for latency.
 struct Item {
   int k_items, v_items, ring_items;
+  int v_tiles, r_tokens;   // totals
+  int vt, rt;              // tiles / tokens per workgroup
 };
 
 // Key row of position p: the appended tokens for p >= new0, else the ring
@@ -88,29 +94,31 @@ __device__ inline void load_chans(const __half* src, float* out) {
   }
 }
 
-// K-group item: threads = output byte column t (the cpt channels of one
-// byte of a plane row) x token slice qt (G / NQ consecutive tokens).  Each
-// thread takes the min/max of its slice, the slices meet in LDS, and each
-// thread then writes the codes of its slice.  A wave's loads cover whole
-// token rows (coalesced) and the token loops are unrolled so several rows
-// are in flight.
+// K-group item: threads = channel column t (8 consecutive channels, one
+// 16-byte load per token row) x token slice qt (G / NQ consecutive tokens).
+// Each thread takes the min/max of its slice, the slices meet in LDS, and
+// each thread then writes its slice's codes: the 8 channels' codes are one
+// whole word of a plane row (a dword for 8-bit codes in nibble planes, 16
+// bits for 2-bit, a byte for 1-bit).  The token loops are unrolled so
+// several rows are in flight.
 template <int W>   // bits per code in a plane: 4 (8-bit codes), 2, 1
 __device__ void key_group(const AppendArgs& a, int item, int b, int kvh,
                           float* s_mn, float* s_mx) {
   const CacheGeom& g = a.g;
-  constexpr int cpt = 8 / W;                  // channels per output byte
+  constexpr int CH = 8;                       // channels per thread
   constexpr int BITS = W == 4 ? 8 : W;
-  const int cols = g.d / cpt;                 // byte columns (16..64)
-  const int nq = kThreads / cols;             // token slices (4..16)
-  const int tpq = g.G / nq;                   // tokens per slice (>= 2)
+  const int cols = g.d / CH;                  // channel columns (8 or 16)
+  const int nq = kThreads / cols;             // token slices (16 or 32)
+  const int tpq = g.G / nq;                   // tokens per slice (>= 1)
   const int t = threadIdx.x % cols, qt = threadIdx.x / cols;
+  const int c0 = t * CH;
   constexpr int Lv = (1 << BITS) - 1;
   const int64_t p0 = a.q0 + (int64_t)item * g.G;
   const int64_t ps = p0 + (int64_t)qt * tpq;
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
-  float mn[8], mx[8], x[8], s[8], z[8];
+  float mn[CH], mx[CH], x[CH], s[CH], z[CH];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) { mn[k] = INFINITY; mx[k] = -INFINITY; }
+  for (int k = 0; k < CH; ++k) { mn[k] = INFINITY; mx[k] = -INFINITY; }
   const int slot0 = (int)(ps % g.ring);        // ring slot of ps (one divide)
   auto slot_of = [&](int tok) {                 // (slot0 + tok) mod ring
     int sl = slot0 + tok;
@@ -119,55 +127,55 @@ __device__ void key_group(const AppendArgs& a, int item, int b, int kvh,
   };
 #pragma unroll 8
   for (int tok = 0; tok < tpq; ++tok) {
-    load_chans<cpt>(key_row(a, b, kvh, ps + tok, slot_of(tok)) + t * cpt, x);
+    load_chans<CH>(key_row(a, b, kvh, ps + tok, slot_of(tok)) + c0, x);
 #pragma unroll
-    for (int k = 0; k < cpt; ++k) {
+    for (int k = 0; k < CH; ++k) {
       mn[k] = fminf(mn[k], x[k]);
       mx[k] = fmaxf(mx[k], x[k]);
     }
   }
 #pragma unroll
-  for (int k = 0; k < cpt; ++k) {
-    s_mn[qt * g.d + t * cpt + k] = mn[k];
-    s_mx[qt * g.d + t * cpt + k] = mx[k];
+  for (int k = 0; k < CH; ++k) {
+    s_mn[qt * g.d + c0 + k] = mn[k];
+    s_mx[qt * g.d + c0 + k] = mx[k];
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < cpt; ++k) {
+  for (int k = 0; k < CH; ++k) {
     float lo = INFINITY, hi = -INFINITY;
     for (int r = 0; r < nq; ++r) {
-      lo = fminf(lo, s_mn[r * g.d + t * cpt + k]);
-      hi = fmaxf(hi, s_mx[r * g.d + t * cpt + k]);
+      lo = fminf(lo, s_mn[r * g.d + c0 + k]);
+      hi = fmaxf(hi, s_mx[r * g.d + c0 + k]);
     }
     z[k] = lo;
     s[k] = stored_scale(lo, hi, Lv);
   }
   if (qt == 0) {
-    __half2* ksz = a.p.k_sz + blk * g.ksz_block + (p0 / g.G) * g.d + t * cpt;
+    __half2* ksz = a.p.k_sz + blk * g.ksz_block + (p0 / g.G) * g.d + c0;
 #pragma unroll
-    for (int k = 0; k < cpt; ++k)
+    for (int k = 0; k < CH; ++k)
       ksz[k] = __halves2half2(__float2half_rn(s[k]), __float2half_rn(z[k]));
   }
-  uint8_t* hi = a.p.k_hi + blk * g.k_block_bytes + t;
-  uint8_t* lo = BITS == 8 ? a.p.k_lo + blk * g.k_block_bytes + t : nullptr;
+  // byte offset of the column's word in a plane row
+  uint8_t* hi = a.p.k_hi + blk * g.k_block_bytes + c0 * W / 8;
+  uint8_t* lo = BITS == 8 ? a.p.k_lo + blk * g.k_block_bytes + c0 * W / 8 : nullptr;
   // codes in batches of KB tokens: the batch's rows are loaded before its
   // codes are stored (the compiler cannot reorder a load above a store that
   // may alias it, so token-by-token the loads would wait in turn)
   constexpr int KB = 8;
   for (int t0 = 0; t0 < tpq; t0 += KB) {
-    float xb[KB][8];
+    float xb[KB][CH];
 #pragma unroll
     for (int u = 0; u < KB; ++u)
       if (t0 + u < tpq)
-        load_chans<cpt>(key_row(a, b, kvh, ps + t0 + u, slot_of(t0 + u)) + t * cpt,
-                        xb[u]);
+        load_chans<CH>(key_row(a, b, kvh, ps + t0 + u, slot_of(t0 + u)) + c0, xb[u]);
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       if (t0 + u >= tpq) break;
       const int64_t p = ps + t0 + u;
       unsigned bh = 0, bl = 0;
 #pragma unroll
-      for (int k = 0; k < cpt; ++k) {
+      for (int k = 0; k < CH; ++k) {
         unsigned q = code_of(xb[u][k], z[k], s[k], Lv);
         if constexpr (BITS == 8) {
           bh |= (q >> 4) << (4 * k);
@@ -176,8 +184,14 @@ __device__ void key_group(const AppendArgs& a, int item, int b, int kvh,
           bh |= q << (W * k);
         }
       }
-      hi[p * g.k_row_bytes] = (uint8_t)bh;
-      if (lo) lo[p * g.k_row_bytes] = (uint8_t)bl;
+      if constexpr (W == 4) {
+        *(unsigned*)(hi + p * g.k_row_bytes) = bh;
+        *(unsigned*)(lo + p * g.k_row_bytes) = bl;
+      } else if constexpr (W == 2) {
+        *(unsigned short*)(hi + p * g.k_row_bytes) = (unsigned short)bh;
+      } else {
+        hi[p * g.k_row_bytes] = (uint8_t)bh;
+      }
     }
   }
 }
@@ -207,11 +221,20 @@ __device__ void value_tile(const AppendArgs& a, int item, int b, int kvh,
   const int64_t p = p0 + j;
   const int slot = (int)(p % g.ring);           // one divide per thread
   float x[16];
+  if (p >= a.new0) {   // appended token: token-major, 16-byte loads
+    const __half* src =
+        a.v_new + (((int64_t)b * a.n + (p - a.new0)) * g.Hkv + kvh) * g.d + c0;
+    load_chans<8>(src, x);
+    if (cpv == 16) load_chans<8>(src + 8, x + 8);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k < cpv) x[k] = value_at(a, b, kvh, p, slot, c0 + k);
+  }
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     if (k < cpv) {
-      x[k] = value_at(a, b, kvh, p, slot, c0 + k);
       mn = fminf(mn, x[k]);
       mx = fmaxf(mx, x[k]);
     }
@@ -289,9 +312,23 @@ append_kernel(AppendArgs a, Item it) {
     return;
   }
   x -= it.k_items;
-  if (x < it.v_items) { value_tile(a, x, b, kvh, lds_hi, lds_lo); return; }
+  if (x < it.v_items) {
+    for (int k = 0; k < it.vt; ++k) {
+      const int tl = x * it.vt + k;
+      if (tl >= it.v_tiles) break;              // uniform in the workgroup
+      if (k > 0) __syncthreads();               // LDS of the last tile read out
+      value_tile(a, tl, b, kvh, lds_hi, lds_lo);
+    }
+    return;
+  }
   x -= it.v_items;
-  if (x < it.ring_items) ring_token(a, x, b, kvh);
+  if (x < it.ring_items) {
+    for (int k = 0; k < it.rt; ++k) {
+      const int r = x * it.rt + k;
+      if (r >= it.r_tokens) break;
+      ring_token(a, r, b, kvh);
+    }
+  }
 }
 
 }  // namespace
@@ -300,8 +337,12 @@ hipError_t launch_append(const AppendArgs& a, bool flush, bool ring_write,
                          hipStream_t s) {
   Item it;
   it.k_items = flush ? a.groups : 0;
-  it.v_items = flush ? (int)((int64_t)a.groups * a.g.G / kTile) : 0;
-  it.ring_items = ring_write ? a.wr_count : 0;
+  it.v_tiles = flush ? (int)((int64_t)a.groups * a.g.G / kTile) : 0;
+  it.r_tokens = ring_write ? a.wr_count : 0;
+  it.vt = it.v_tiles >= 64 ? 4 : 1;
+  it.rt = it.r_tokens >= 64 ? 8 : 1;
+  it.v_items = (int)cdiv(it.v_tiles, it.vt);
+  it.ring_items = (int)cdiv(it.r_tokens, it.rt);
   const int64_t nx = (int64_t)it.k_items + it.v_items + it.ring_items;
   if (nx == 0) return hipSuccess;
   dim3 grid((unsigned)nx, a.g.Hkv, a.g.B);
