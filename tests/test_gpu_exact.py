@@ -170,3 +170,25 @@ def test_specache_pipeline_full_size():
         lerr = np.abs(lse[b:b + 1, h * gs:(h + 1) * gs] - ref_lse)
         say(f"    ({b},{h}): rel err {rel:.2e}, lse err {lerr.max():.2e}")
         assert (lerr <= tol).all(), (b, h)
+
+
+def test_verify_exact_without_substitutions_equals_verify():
+    """No fetched rows (n = 0), or only skipped entries (-1): the
+    substitution partial is empty (m = -inf, l = 0, o = 0), so the merge adds
+    exact zeros and out and lse equal plain verify bit for bit."""
+    w = CASES[2][1]
+    say("[gpu] exact verify with nothing substituted")
+    shape = shape_for(w)
+    cache = kq.QuantKVCache(shape)
+    K, V = host_tokens(w, 3)
+    cache.append(to_dev(K), to_dev(V))
+    q = to_dev(synth.queries(w, 4, 7))
+    ref, ref_lse = cache.verify(q, want_lse=True)
+    for n, fill in ((0, 0), (5, -1)):
+        idx = torch.full((w.B, w.Hkv, n), fill, dtype=torch.int32, device="cuda")
+        kx = torch.zeros((w.B, w.Hkv, n, w.d), dtype=torch.float16, device="cuda")
+        out, lse = cache.verify_exact(q, idx, kx, kx.clone(), t_exact=0,
+                                      want_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), n
+        assert torch.equal(lse, ref_lse), n
