@@ -28,6 +28,11 @@ CASES = [
      "target", 3, 1),
     ("mha_d64", W("mha_d64_int8", 1, 3, 3, 64, 777, 64, 32, 128, 8, "outlier"),
      "target", 2, 0),
+    # T = 16: the substituted row is the last of 32 rows, or a middle one
+    ("gqa2_t16_last", W("gqa2", 1, 4, 2, 128, 900, 64, 64, 128, 8, "outlier"),
+     "target", 16, 15),
+    ("mha_d64_t16_draft", W("mha_d64_int8", 1, 3, 3, 64, 777, 64, 32, 128, 8,
+                            "outlier"), "draft4", 16, 7),
 ]
 
 

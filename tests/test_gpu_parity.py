@@ -33,6 +33,8 @@ SMALL = {
     # top-k's 1024-token chunks
     "g96": W("g96", 1, 8, 2, 128, 2400, 96, 64, 192, 8, "outlier"),
     "g96_2bit": W("g96_2bit", 1, 8, 2, 128, 2000, 96, 32, 96, 2, "normal"),
+    # two query heads per kv head: T = 16 fills the 32-row limit
+    "gqa2": W("gqa2", 1, 4, 2, 128, 900, 64, 64, 128, 8, "outlier"),
 }
 
 
@@ -110,7 +112,10 @@ RUNS = [("tiny", "target", 1), ("tiny", "draft4", 1), ("tiny", "target", 8),
         ("gqa_2bit", "target", 2), ("gqa_2bit", "target", 8),
         ("gqa_1bit", "target", 2), ("d64_2bit", "target", 5),
         ("gv128", "target", 4), ("gv128", "draft4", 8),
-        ("g96", "target", 7), ("g96", "draft4", 1), ("g96_2bit", "target", 2)]
+        ("g96", "target", 7), ("g96", "draft4", 1), ("g96_2bit", "target", 2),
+        # T = 16, the largest speculative block: 16 rows (MHA) and 32 (GQA 2)
+        ("mha_d64_int8", "target", 16), ("gqa2", "target", 16),
+        ("gqa2", "draft4", 16)]
 
 
 @pytest.mark.parametrize("name,path,T", RUNS)
