@@ -110,6 +110,15 @@ __device__ void sort_regs_desc(unsigned long long (&e)[TPT],
   }
 }
 
+// Code of channel cc of a 1/2-bit code dword as a float, from the dword
+// masked to one code per byte: mw[r] = (h >> (W * r)) & (one code mask in
+// each byte), so channel cc = (8 / W) * byte + r sits in byte cc / (8 / W)
+// of mw[cc % (8 / W)] and converts with one byte-to-float instruction.
+template <int W>
+__device__ __forceinline__ float code_bytes(const unsigned (&mw)[8 / W], int cc) {
+  return (float)((mw[cc % (8 / W)] >> (8 * (cc / (8 / W)))) & 0xFFu);
+}
+
 // Code of channel cc of a code dword (hi plane; lo plane for 8-bit), per
 // path, as a float.
 template <int BITS, int PATH>
@@ -165,56 +174,133 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
   const uint8_t* kh = a.p.k_hi + blk * g.k_block_bytes;
   const uint8_t* kl = LO ? a.p.k_lo + blk * g.k_block_bytes : nullptr;
 
-  // thread t scores tokens t, t + 256, t + 512, t + 768 of the chunk (one
-  // code row load per wave is one contiguous span)
   unsigned long long comp[TPT];
-#pragma unroll 1
-  for (int m = 0; m < TPT; ++m) {
-    const int64_t j = c0 + m * NT + tid;
-    unsigned long long cm = 0ull;                // below every real key
-    if (j < a.n_q) {
-      unsigned hw[NDW], lw[LO ? NDW : 1];
+  if constexpr (BITS != 8) {
+    // 1/2-bit codes: thread t scores the 4 consecutive tokens 4t .. 4t + 3
+    // of the chunk together.  They share one key group (G is a multiple of
+    // 32), so each channel's q and (s, z) come out of LDS once for all four
+    // tokens; every token's sum still runs over c = 0..d-1 in order.  n_q is
+    // a multiple of G, so the four are valid together or not at all.
+    const int64_t j0 = c0 + TPT * tid;
+    if (j0 < a.n_q) {
+      unsigned hw[TPT][NDW];
 #pragma unroll
-      for (int x = 0; x < NDW / 4; ++x) {
-        const uint4 v = ((const uint4*)(kh + j * (NDW * 4)))[x];
-        hw[4 * x] = v.x; hw[4 * x + 1] = v.y; hw[4 * x + 2] = v.z; hw[4 * x + 3] = v.w;
-        if constexpr (LO) {
-          const uint4 u = ((const uint4*)(kl + j * (NDW * 4)))[x];
-          lw[4 * x] = u.x; lw[4 * x + 1] = u.y; lw[4 * x + 2] = u.z; lw[4 * x + 3] = u.w;
+      for (int x = 0; x < NDW / 4; ++x)
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) {
+          const uint4 v = ((const uint4*)(kh + (j0 + m) * (NDW * 4)))[x];
+          hw[m][4 * x] = v.x; hw[m][4 * x + 1] = v.y;
+          hw[m][4 * x + 2] = v.z; hw[m][4 * x + 3] = v.w;
         }
-      }
-      const float2* sz = s_sz + (int)(j / g.G - gi0) * SZR;
-      float acc[GS];
+      const float2* sz = s_sz + (int)(j0 / g.G - gi0) * SZR;
+      float acc[TPT][GS];
 #pragma unroll
-      for (int h = 0; h < GS; ++h) acc[h] = 0.f;
-      // channels in order, one code dword per iteration; the dwords move
-      // down a register window so the loop stays rolled (unrolled, every
-      // channel's LDS reads would be hoisted and hold the registers)
+      for (int m = 0; m < TPT; ++m)
+#pragma unroll
+        for (int h = 0; h < GS; ++h) acc[m][h] = 0.f;
+      // one code dword per token per iteration; the dwords move down a
+      // register window so the loop stays rolled
 #pragma unroll 1
       for (int x = 0; x < NDW; ++x) {
-        const unsigned h0 = hw[0], l0 = LO ? lw[0] : 0u;
+        unsigned h0[TPT];
 #pragma unroll
-        for (int i = 0; i + 1 < NDW; ++i) {
-          hw[i] = hw[i + 1];
-          if constexpr (LO) lw[i] = lw[i + 1];
+        for (int m = 0; m < TPT; ++m) {
+          h0[m] = hw[m][0];
+#pragma unroll
+          for (int i = 0; i + 1 < NDW; ++i) hw[m][i] = hw[m][i + 1];
         }
+        constexpr unsigned BM = BITS == 2 ? 0x03030303u : 0x01010101u;
+        unsigned mw[TPT][8 / BITS];
+#pragma unroll
+        for (int m = 0; m < TPT; ++m)
+#pragma unroll
+          for (int r = 0; r < 8 / BITS; ++r) {
+            mw[m][r] = (h0[m] >> (BITS * r)) & BM;
+            // opaque to the optimizer, which would otherwise fold the mask
+            // back into one bit-field extract per channel
+            asm("" : "+v"(mw[m][r]));
+          }
 #pragma unroll
         for (int cc = 0; cc < CPD; ++cc) {
           const int c = x * CPD + cc;
-          const float code = code_of<BITS, PATH>(h0, l0, cc);
           const float2 p = sz[c];                // (s, z)
-          const float kc = p.y + code * p.x;
+          float qc[GS];
 #pragma unroll
-          for (int h = 0; h < GS; ++h) acc[h] = acc[h] + s_q[c][h] * kc;
+          for (int h = 0; h < GS; ++h) qc[h] = s_q[c][h];
+#pragma unroll
+          for (int m = 0; m < TPT; ++m) {
+            // z + code * s with code * s exact (a code of <= 8 bits times
+            // an fp16 scale fits binary32), so one fused op rounds the same
+            const float kc = __builtin_fmaf(code_bytes<BITS>(mw[m], cc), p.x, p.y);
+#pragma unroll
+            for (int h = 0; h < GS; ++h) acc[m][h] = acc[m][h] + qc[h] * kc;
+          }
         }
       }
-      float key = acc[0];
 #pragma unroll
-      for (int h = 1; h < GS; ++h) key = fmaxf(key, acc[h]);
-      key = key + 0.f;
-      cm = composite(key, j);
+      for (int m = 0; m < TPT; ++m) {
+        float key = acc[m][0];
+#pragma unroll
+        for (int h = 1; h < GS; ++h) key = fmaxf(key, acc[m][h]);
+        key = key + 0.f;
+        comp[m] = composite(key, j0 + m);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < TPT; ++m) comp[m] = 0ull;   // below every real key
     }
-    comp[m] = cm;
+  } else {
+    // 8-bit codes: thread t scores tokens t, t + 256, t + 512, t + 768 of the
+    // chunk one at a time (one code row load per wave is one contiguous span)
+#pragma unroll 1
+    for (int m = 0; m < TPT; ++m) {
+      const int64_t j = c0 + m * NT + tid;
+      unsigned long long cm = 0ull;                // below every real key
+      if (j < a.n_q) {
+        unsigned hw[NDW], lw[LO ? NDW : 1];
+#pragma unroll
+        for (int x = 0; x < NDW / 4; ++x) {
+          const uint4 v = ((const uint4*)(kh + j * (NDW * 4)))[x];
+          hw[4 * x] = v.x; hw[4 * x + 1] = v.y; hw[4 * x + 2] = v.z; hw[4 * x + 3] = v.w;
+          if constexpr (LO) {
+            const uint4 u = ((const uint4*)(kl + j * (NDW * 4)))[x];
+            lw[4 * x] = u.x; lw[4 * x + 1] = u.y; lw[4 * x + 2] = u.z; lw[4 * x + 3] = u.w;
+          }
+        }
+        const float2* sz = s_sz + (int)(j / g.G - gi0) * SZR;
+        float acc[GS];
+#pragma unroll
+        for (int h = 0; h < GS; ++h) acc[h] = 0.f;
+        // channels in order, one code dword per iteration; the dwords move
+        // down a register window so the loop stays rolled (unrolled, every
+        // channel's LDS reads would be hoisted and hold the registers)
+#pragma unroll 1
+        for (int x = 0; x < NDW; ++x) {
+          const unsigned h0 = hw[0], l0 = LO ? lw[0] : 0u;
+#pragma unroll
+          for (int i = 0; i + 1 < NDW; ++i) {
+            hw[i] = hw[i + 1];
+            if constexpr (LO) lw[i] = lw[i + 1];
+          }
+#pragma unroll
+          for (int cc = 0; cc < CPD; ++cc) {
+            const int c = x * CPD + cc;
+            const float code = code_of<BITS, PATH>(h0, l0, cc);
+            const float2 p = sz[c];                // (s, z)
+            // z + code * s, code * s exact: one fused op rounds the same
+            const float kc = __builtin_fmaf(code, p.x, p.y);
+#pragma unroll
+            for (int h = 0; h < GS; ++h) acc[h] = acc[h] + s_q[c][h] * kc;
+          }
+        }
+        float key = acc[0];
+#pragma unroll
+        for (int h = 1; h < GS; ++h) key = fmaxf(key, acc[h]);
+        key = key + 0.f;
+        cm = composite(key, j);
+      }
+      comp[m] = cm;
+    }
   }
 
   sort_regs_desc<NT>(comp, s_x);
