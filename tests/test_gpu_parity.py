@@ -35,6 +35,10 @@ SMALL = {
     "g96_2bit": W("g96_2bit", 1, 8, 2, 128, 2000, 96, 32, 96, 2, "normal"),
     # two query heads per kv head: T = 16 fills the 32-row limit
     "gqa2": W("gqa2", 1, 4, 2, 128, 900, 64, 64, 128, 8, "outlier"),
+    # bulk appends of many small key groups with a flush count that is not
+    # a multiple of 4 or 2: 81 groups of 32 and 71 groups of 64
+    "g32_bulk": W("g32_bulk", 1, 4, 2, 128, 2600, 32, 32, 32, 2, "normal"),
+    "g64_bulk": W("g64_bulk", 1, 4, 2, 128, 4560, 64, 64, 64, 8, "outlier"),
 }
 
 
