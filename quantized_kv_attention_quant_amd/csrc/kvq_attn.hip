@@ -392,8 +392,50 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
 // the kv group share the loaded rows.  Each wave keeps (m, l, o) per head
 // with the usual rescaling, and the 16 wave states meet in LDS by
 // log-sum-exp.  Skipped entries read stand-in position 0 and are never
-// folded in.
-template <int D, int RP>
+// folded in.  The code width W is a template parameter and every division
+// in the element addressing is a shift (Gv divides d, a power of two) except
+// one 32-bit divide per token for its key group: there is no integer divide
+// instruction, and per-element software divides made the kernel ALU-bound.
+
+// Dequantized key and value element (channel c) of quantized token pos of
+// block blk, from the documented layouts: key group grp = pos / G, value
+// tile pos / 32.
+template <int W, int D>
+__device__ inline float2 exact_kv_deq(const AttnArgs& a, int64_t blk, int pos,
+                                      int grp, int c, int gv_sh, bool draft) {
+  const CacheGeom& g = a.g;
+  constexpr bool TWO = W == 4;                   // 8-bit codes: two planes
+  constexpr unsigned MASK = (1u << W) - 1u;
+  constexpr int PB = 8 / W;                      // key codes per byte
+  // key: byte c / PB of the token's plane row, bits W * (c % PB)
+  const int64_t row = blk * g.k_block_bytes + (int64_t)pos * g.k_row_bytes + c / PB;
+  const int ksh = W * (c % PB);
+  const unsigned khi = ((unsigned)a.p.k_hi[row] >> ksh) & MASK;
+  const unsigned klo = TWO ? ((unsigned)a.p.k_lo[row] >> ksh) & MASK : 0u;
+  const __half2 ksz = a.p.k_sz[blk * g.ksz_block + (int64_t)grp * D + c];
+  // value: token j of its 32-token tile, dword (16 jg + r) (D W / 64) + m / per
+  // of the tile, bits 16 jh + W (4 (m % per) + ji)
+  constexpr int PER = 4 / W;
+  const int j = pos % kTile, jg = (j % 16) / 4, ji = j % 4, jh = j / 16;
+  const int r = c % 16, m = c / 16;
+  const int dw = (16 * jg + r) * (D * W / 64) + m / PER;
+  const int vsh = 16 * jh + W * (4 * (m % PER) + ji);
+  const int64_t tile = blk * g.v_block_bytes + (int64_t)(pos / kTile) * g.v_tile_bytes;
+  const unsigned vhi = (((const uint32_t*)(a.p.v_hi + tile))[dw] >> vsh) & MASK;
+  const unsigned vlo = TWO ? (((const uint32_t*)(a.p.v_lo + tile))[dw] >> vsh) & MASK : 0u;
+  // the value group's (s, z): halves [part][g][i][group][h] of the tile
+  const int ngv = D >> gv_sh, gg = c >> gv_sh;
+  const __half* t = (const __half*)(a.p.v_sz + blk * g.vsz_block +
+                                    (int64_t)(pos / kTile) * g.vsz_tile);
+  const int so = (jg * 4 + ji) * ngv * 2 + gg * 2 + jh;
+  const int zo = ((4 + jg) * 4 + ji) * ngv * 2 + gg * 2 + jh;
+  const float kc = code_value(khi, klo, TWO, draft);
+  const float vc = code_value(vhi, vlo, TWO, draft);
+  return make_float2(__high2float(ksz) + kc * __low2float(ksz),
+                     __half2float(t[zo]) + vc * __half2float(t[so]));
+}
+
+template <int D, int RP, int W>
 __global__ void __launch_bounds__(1024) exact_kernel(const AttnArgs a) {
   constexpr int NT = 1024, HB = 4;               // heads per workgroup
   constexpr int NWV = NT / kWave, CPL = D / kWave;
@@ -412,6 +454,7 @@ __global__ void __launch_bounds__(1024) exact_kernel(const AttnArgs a) {
   float* po = a.ws + (blk * a.s_alloc + a.S) * pstride;
   const __half* ke = a.k_exact + blk * n * D;
   const __half* ve = a.v_exact + blk * n * D;
+  const int gv_sh = __builtin_ctz((unsigned)g.Gv);   // Gv is a power of two
 
   // empty partials for these heads' other query rows
   for (int t = 0; t < a.T; ++t) {
@@ -451,16 +494,16 @@ __global__ void __launch_bounds__(1024) exact_kernel(const AttnArgs a) {
       const int i = i0 + u * NWV;
       const int64_t p = i < n ? s_idx[i] : -1;
       ok[u] = p >= 0 && p < a.n_q;
-      const int64_t ps = ok[u] ? p : 0;        // stand-in: never folded in
+      const int ps = ok[u] ? (int)p : 0;       // stand-in: never folded in
+      const int grp = (int)((unsigned)ps / (unsigned)g.G);   // n_q < 2^24
       const int64_t is = i < n ? i : 0;
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
         const int c = lane + kWave * k;
-        const __half2 sz = key_sz(g, a.p, blk, ps, c);
-        kq[u][k] = __high2float(sz) + key_code(g, a.p, blk, ps, c, draft) * __low2float(sz);
+        const float2 kv = exact_kv_deq<W, D>(a, blk, ps, grp, c, gv_sh, draft);
+        kq[u][k] = kv.x;
         kx[u][k] = __half2float(ke[is * D + c]);
-        const float2 vs = value_sz(g, a.p, blk, ps, c);
-        vq[u][k] = vs.y + value_code(g, a.p, blk, ps, c, draft) * vs.x;
+        vq[u][k] = kv.y;
         vx[u][k] = __half2float(ve[is * D + c]);
       }
     }
@@ -1289,9 +1332,13 @@ hipError_t go(AttnArgs a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.n_exact >= 0) {
-    hipLaunchKernelGGL((exact_kernel<D, C::RP>),
-                       dim3((unsigned)cdiv(a.gs, 4), (unsigned)a.g.Hkv, (unsigned)a.g.B),
-                       dim3(1024), 0, s, a);
+    const dim3 xg((unsigned)cdiv(a.gs, 4), (unsigned)a.g.Hkv, (unsigned)a.g.B);
+    if (a.g.w == 4)
+      hipLaunchKernelGGL((exact_kernel<D, C::RP, 4>), xg, dim3(1024), 0, s, a);
+    else if (a.g.w == 2)
+      hipLaunchKernelGGL((exact_kernel<D, C::RP, 2>), xg, dim3(1024), 0, s, a);
+    else
+      hipLaunchKernelGGL((exact_kernel<D, C::RP, 1>), xg, dim3(1024), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     ++a.S;                       // the merge reads the substitution partial too
