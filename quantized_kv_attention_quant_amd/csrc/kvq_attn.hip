@@ -386,11 +386,12 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
 // the S + 1 partials then removes each fetched token's quantized term and
 // adds its exact one.  The other query rows of those heads get an empty
 // partial (m = -inf, l = 0, o = 0).  Positions outside [0, n_q) are skipped.
-// 1024 threads: each wave takes fetched tokens w, w + 16, ... with its lanes
+// 512 threads, two workgroups per CU (so a batched call's workgroups run in
+// one round): each wave takes fetched tokens w, w + 8, ... with its lanes
 // over the channels and issues all K and V loads of UT tokens together (the
 // positions are scattered, so each round of loads is long); the heads of
 // the kv group share the loaded rows.  Each wave keeps (m, l, o) per head
-// with the usual rescaling, and the 16 wave states meet in LDS by
+// with the usual rescaling, and the 8 wave states meet in LDS by
 // log-sum-exp.  Skipped entries read stand-in position 0 and are never
 // folded in.  The code width W is a template parameter and every division
 // in the element addressing is a shift (Gv divides d, a power of two) except
@@ -436,8 +437,8 @@ __device__ inline float2 exact_kv_deq(const AttnArgs& a, int64_t blk, int pos,
 }
 
 template <int D, int RP, int W>
-__global__ void __launch_bounds__(1024) exact_kernel(const AttnArgs a) {
-  constexpr int NT = 1024, HB = 4;               // heads per workgroup
+__global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
+  constexpr int NT = 512, HB = 4;                // heads per workgroup
   constexpr int NWV = NT / kWave, CPL = D / kWave;
   constexpr int UT = CPL == 1 ? 4 : 2;          // tokens a wave loads together
   __shared__ float s_q[HB][D];
@@ -1334,11 +1335,11 @@ hipError_t go(AttnArgs a, hipStream_t s) {
   if (a.n_exact >= 0) {
     const dim3 xg((unsigned)cdiv(a.gs, 4), (unsigned)a.g.Hkv, (unsigned)a.g.B);
     if (a.g.w == 4)
-      hipLaunchKernelGGL((exact_kernel<D, C::RP, 4>), xg, dim3(1024), 0, s, a);
+      hipLaunchKernelGGL((exact_kernel<D, C::RP, 4>), xg, dim3(512), 0, s, a);
     else if (a.g.w == 2)
-      hipLaunchKernelGGL((exact_kernel<D, C::RP, 2>), xg, dim3(1024), 0, s, a);
+      hipLaunchKernelGGL((exact_kernel<D, C::RP, 2>), xg, dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((exact_kernel<D, C::RP, 1>), xg, dim3(1024), 0, s, a);
+      hipLaunchKernelGGL((exact_kernel<D, C::RP, 1>), xg, dim3(512), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     ++a.S;                       // the merge reads the substitution partial too
