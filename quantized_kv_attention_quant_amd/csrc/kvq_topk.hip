@@ -61,11 +61,13 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x,
 // 4 * tid + m in e[m].  Element i meets i ^ j at stage (k, j); the pair is
 // put in descending order when (i & k) == 0, ascending otherwise, so the
 // run of every stage k ends ordered and the last one sorts all elements.
+// Runs of k_first / 2 elements that already stand in that order (even runs
+// descending, odd runs ascending) may skip the stages below k_first.
 template <int NTS>
 __device__ void sort_regs_desc(unsigned long long (&e)[TPT],
-                               unsigned long long* lds) {
+                               unsigned long long* lds, int k_first = 2) {
   const int tid = threadIdx.x;
-  for (int k = 2; k <= NTS * TPT; k <<= 1) {
+  for (int k = k_first; k <= NTS * TPT; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       if (j < TPT) {                      // both elements in this thread
 #pragma unroll
@@ -322,12 +324,17 @@ __global__ void __launch_bounds__(NTM) merge_kernel(const TopkArgs a) {
   const unsigned long long* all = a.cand + blk * a.chunks * a.k;
   const int total = a.chunks * a.k;
   unsigned long long e[TPT];
+  // each chunk's k candidates are sorted descending; for k a power of two
+  // the chunk lists fill whole runs of the network, so loading every odd
+  // list reversed gives the state after its stages below 2k
+  const bool runs = (a.k & (a.k - 1)) == 0;
 #pragma unroll
   for (int m = 0; m < TPT; ++m) {
     const int i = TPT * tid + m;
-    e[m] = i < total ? all[i] : 0ull;
+    const int r = i / a.k, src = runs && (r & 1) ? r * a.k + (a.k - 1 - i % a.k) : i;
+    e[m] = i < total ? all[src] : 0ull;
   }
-  sort_regs_desc<NTM>(e, s_x);
+  sort_regs_desc<NTM>(e, s_x, runs ? 2 * a.k : 2);
   for (int taken = cap; taken < total; taken += cap - a.k) {
 #pragma unroll
     for (int m = 0; m < TPT; ++m) {

@@ -39,6 +39,8 @@ SMALL = {
     # a multiple of 4 or 2: 81 groups of 32 and 71 groups of 64
     "g32_bulk": W("g32_bulk", 1, 4, 2, 128, 2600, 32, 32, 32, 2, "normal"),
     "g64_bulk": W("g64_bulk", 1, 4, 2, 128, 4560, 64, 64, 64, 8, "outlier"),
+    # 10 top-k chunks: top-256 candidates overflow one merge pass
+    "long_2bit": W("long_2bit", 1, 8, 2, 128, 9500, 32, 32, 32, 2, "normal"),
 }
 
 
@@ -191,7 +193,8 @@ def test_verify_row_equals_prefix_decode():
     ("gqa_d128_int8", "target", 64), ("gqa_d128_int8", "draft4", 64),
     ("gqa_2bit", "target", 64), ("gqa_1bit", "target", 100),
     ("mha_d64_int8", "target", 256), ("tiny", "target", 300 // 2),
-    ("g96", "target", 64), ("g96", "draft4", 64), ("g96_2bit", "target", 200)])
+    ("g96", "target", 64), ("g96", "draft4", 64), ("g96_2bit", "target", 200),
+    ("g32_bulk", "target", 128), ("long_2bit", "target", 256)])
 def test_topk_bit_exact(name, path, k):
     w = SMALL[name]
     say(f"[gpu] topk {name} {path} k={k}")
