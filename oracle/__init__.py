@@ -30,5 +30,9 @@ Sources (cited by page title and section):
       only the needed subsets reconstructed on demand).
 
 Parity status (which function is pinned by what) is listed in each module's
-docstring.  Nothing here is unpinned.
+docstring.  Every function is pinned against values the pages or the
+mathematics fix; the two binary32 definitions that decide integers (the
+quantizer's correctly rounded quotient and the top-k key's sequential,
+unfused channel sum) are pinned by hand-derived goldens that a plausible
+alternative (reciprocal-multiply, pairwise or fused sum) fails.
 """

@@ -21,6 +21,11 @@ Pinned by (tests/test_oracle_quant.py): code range, end codes hitting 0 and
 Lv in every non-degenerate group, |x - x^| <= s/2 (1 + 2^-9),
 |x - x^4| <= 8 s (1 + 2^-9), degenerate groups, the grouping axes, and a
 hand-derived worked example (tests/golden/quant_worked_example.json).
+Pinned to the bit by (tests/test_oracle_bitlevel.py): two hand-derived
+groups whose quotient (x - z)/s is an exact half-integer, where a
+reciprocal-multiply would give another code
+(tests/golden/quant_divide_ties.json), and a scalar pure-Python loop over
+the tiny workload at 1, 2 and 8 bits.
 """
 from __future__ import annotations
 

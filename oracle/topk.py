@@ -22,6 +22,9 @@ Pinned by (tests/test_oracle_topk.py): brute force on tiny shapes (Python
 sorted over exact rational scores when they are far apart), agreement with
 torch.topk over float64 softmax probabilities for one head, the binary32
 error bound against the float64 dot product, tie and padding rules.
+Pinned to the bit by (tests/test_oracle_bitlevel.py): two hand-derived
+blocks (tests/golden/topk_key_rounding.json) whose keys and order change if
+the channel sum is taken pairwise or with fused multiply-adds.
 """
 from __future__ import annotations
 
