@@ -12,9 +12,13 @@ One step = one pass of the hot path for a gamma = 6 speculative step:
   kv_attn_verify   INT4 draft attention, T=1 (upper nibble plane only)
   kv_attn_verify   INT8 target verify attention, T=7 (causal among the 7)
   kv_rollback      of the 7 tokens (host counters; the next step reuses them)
-Each step works on a different copy of the layer's cache (8 copies, 0.57 GB)
-so that, as in a model with many layers, a step never finds its cache in the
-256 MB Infinity Cache.
+The layer's cache has 8 copies (0.57 GB), standing for 8 layers of a model.
+Step i appends to and drafts on copy i mod 8, and verifies and rolls back
+copy (i - 4) mod 8, whose draft ran 4 steps earlier: as in a model, where
+the draft pass over every layer runs between a layer's draft and its
+verify, neither attention call finds its cache in the 256 MB Infinity Cache
+(about 430 MB of other copies are read in between).  A verify timed right
+after the draft on the same copy (warm) is reported beside it.
 
 The JSON line reports us/step (wall clock over the timed steps), the
 dominant kernel's duration (HIP events on its stream) against the HBM
@@ -43,6 +47,7 @@ PEAK_GBPS = 8000.0
 WORKLOAD = "llama3_8b_32k"
 T_VERIFY, T_DRAFT = 7, 1
 N_COPIES = 8
+LAG = N_COPIES // 2          # a copy's verify runs LAG steps after its draft
 
 
 def algorithmic_bytes(Hkv, Hq, d, G, Gv, n_q, n_r, T, bits_read):
@@ -89,33 +94,75 @@ def build_caches(w, seed, device):
     return caches, K, V, prefill_us
 
 
-def cpu_baseline(w, seed, K, V, q_draft, q_verify, k_new, v_new,
-                 budget_s=10.0):
-    """Time the CPU oracle on full steps (all 8 kv heads): append the 7
-    tokens to the replayed cache, draft + verify attention in float64,
-    rollback; repeated until ~budget_s of CPU work, one BLAS/OpenMP thread.
-    The replay of the 32K-token prefix is set-up, not timed."""
+def _oracle_steps(args):
+    """One worker of the CPU baseline: replay the prefix of kv heads
+    [h0, h1) (untimed), then run full steps on them until `budget_s` of
+    wall time has passed.  Returns (steps, seconds)."""
+    w, K, V, q_draft, q_verify, k_new, v_new, h0, h1, budget_s = args
     from threadpoolctl import threadpool_limits
     from oracle import attention as oatt
     from oracle import cache as ocache
+    gs = w.Hq // w.Hkv
+    qd = np.ascontiguousarray(q_draft[:, :, h0 * gs:h1 * gs])
+    qv = np.ascontiguousarray(q_verify[:, :, h0 * gs:h1 * gs])
     with threadpool_limits(limits=1):
-        rep = ocache.Replay(w.B, w.Hkv, w.d, w.G, w.Gv, w.bits, w.R)
-        rep.append(K, V)
+        rep = ocache.Replay(w.B, h1 - h0, w.d, w.G, w.Gv, w.bits, w.R)
+        rep.append(np.ascontiguousarray(K[:, :, h0:h1]),
+                   np.ascontiguousarray(V[:, :, h0:h1]))
+        kn = np.ascontiguousarray(k_new[:, :, h0:h1])
+        vn = np.ascontiguousarray(v_new[:, :, h0:h1])
         steps, t0 = 0, time.perf_counter()
         while True:
-            rep.append(k_new, v_new)
-            oatt.attend(rep, q_draft, "draft4", w.d ** -0.5)
-            oatt.attend(rep, q_verify, "target", w.d ** -0.5)
+            rep.append(kn, vn)
+            oatt.attend(rep, qd, "draft4", w.d ** -0.5)
+            oatt.attend(rep, qv, "target", w.d ** -0.5)
             rep.rollback(T_VERIFY)
             steps += 1
             dt = time.perf_counter() - t0
             if dt >= budget_s:
-                break
-    return {"value": round(dt / steps * 1e6, 1), "unit": "us/step",
-            "cores": 1, "kind": "oracle",
-            "sample": f"{steps} full steps (append 7, INT4 draft T=1, INT8 "
-                      "verify T=7 over all 8 kv heads of the 32K cache, "
-                      "rollback 7), float64 numpy, one host thread; prefix "
+                return steps, dt
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, seed, K, V, q_draft, q_verify, k_new, v_new,
+                 budget_s=10.0):
+    """Time the CPU oracle on full steps (append the 7 tokens to the
+    replayed cache, draft + verify attention in float64, rollback) on the
+    host's cores: the 8 kv-head blocks are independent, so P worker
+    processes (P = the cores this process may run on, at most one per kv
+    head and at most 16) each take Hkv/P heads and run steps for
+    ~budget_s; a step takes the slowest worker's time per step.  The
+    oracle's numpy code is unchanged (one BLAS thread per worker).  The
+    replay of the 32K-token prefix is set-up, not timed."""
+    import multiprocessing as mp
+    visible = len(os.sched_getaffinity(0))
+    P = max(1, min(visible, 16, w.Hkv))
+    while w.Hkv % P:
+        P -= 1
+    per = w.Hkv // P
+    jobs = [(w, K, V, q_draft, q_verify, k_new, v_new, i * per, (i + 1) * per,
+             budget_s) for i in range(P)]
+    with mp.get_context("spawn").Pool(P) as pool:
+        res = pool.map(_oracle_steps, jobs)
+    per_step = max(dt / n for n, dt in res)
+    steps = min(n for n, _ in res)
+    return {"value": round(per_step * 1e6, 1), "unit": "us/step",
+            "cores": P, "kind": "oracle",
+            "cpu_model": _cpu_model(), "host_cpus_visible": visible,
+            "sample": f"{steps}+ full steps per worker (append 7, INT4 draft "
+                      "T=1, INT8 verify T=7, rollback 7) over the 32K cache, "
+                      f"{P} worker processes of {per} kv head(s) each, "
+                      "float64 numpy, one BLAS thread per worker; prefix "
                       "replay untimed"}
 
 
@@ -232,9 +279,10 @@ def comparators(w, seed, K, V, caches, q_draft, q_verify, k_new, v_new,
     }
 
 
-def specache_pipeline(seed, steps=30):
-    """The SpeCache-style prefetch path at the batched 32K 2-bit size (B=36,
-    Hq=32, Hkv=8, d=128, G=Gv=R=32, T=2: output token + speculative token):
+def specache_pipeline(seed, name="specache_2bit", steps=30):
+    """The SpeCache-style prefetch path at the batched 32K 1-bit or 2-bit
+    size (B=36, Hq=32, Hkv=8, d=128, G=Gv=R=32, T=2: output token +
+    speculative token):
       kv_topk           top-64 positions per kv head from the speculative
                         token's 2-bit scores
       kv_fetch_rows     those rows' fp16 K and V from a pinned host copy
@@ -245,7 +293,7 @@ def specache_pipeline(seed, steps=30):
     import torch
     import kvq_synth as synth
     import quantized_kv_attention_quant_amd as kq
-    w = synth.WORKLOADS["specache_2bit"]
+    w = synth.WORKLOADS[name]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     g = torch.Generator(device=dev)
@@ -296,8 +344,8 @@ def specache_pipeline(seed, steps=30):
     verify_bytes = w.B * algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv,
                                            cache.n_q, cache.n_r, T, w.bits)
     res = {
-        "workload": "SpeCache-style batched 2-bit cache: B=36 Hq=32 Hkv=8 "
-                    "d=128 L=32768 G=Gv=R=32, T=2, top-64 per kv head",
+        "workload": f"SpeCache-style batched {w.bits}-bit cache: B=36 Hq=32 "
+                    "Hkv=8 d=128 L=32768 G=Gv=R=32, T=2, top-64 per kv head",
         "topk_us": round(us["topk"], 3),
         "fetch_us": round(us["fetch"], 3),
         "fetch_host_gbps": round(fetch_bytes / (us["fetch"] * 1e-6) / 1e9, 2),
@@ -366,6 +414,23 @@ def lwm_128k_steps(seed, steps=64):
                           ws, sh)
         e[1].record(stream)
         d1.append(e)
+    # the INT8 verify at T = 1..6 on the full cache (the T query tokens are
+    # the last T of the residual; 1.1 GB per call, more than the Infinity
+    # Cache, so every call is cold)
+    sweep = {}
+    for T in range(1, 7):
+        qT = torch.from_numpy(synth.queries(w, seed + 20 + T, T)).to(dev)
+        oT = torch.empty_like(qT)
+        ev = []
+        for i in range(12):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            kq.kv_attn_verify(cache.c, qT, T, w.Hq, kq.KVQ_TARGET, sm, oT,
+                              None, ws, sh)
+            e[1].record(stream)
+            if i >= 2:
+                ev.append(e)
+        sweep[T] = ev
     torch.cuda.synchronize()
     app = [(e[0].elapsed_time(e[1]) * 1e3, fl) for e, fl, _, _ in rec]
     ver = [e[1].elapsed_time(e[2]) * 1e3 for e, _, _, _ in rec]
@@ -376,6 +441,8 @@ def lwm_128k_steps(seed, steps=64):
     draft_bytes = algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv, cache.n_q,
                                     cache.n_r, 1, 4)
     flush = [a for a, fl in app if fl]
+    sweep_us = {T: float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in ev]))
+                for T, ev in sweep.items()}
     res = {
         "workload": "LWM-7B-shaped 128K layer: B=1 Hq=Hkv=32 d=128 "
                     "L=131072 G=128 Gv=64 R=256 INT8; steps of append 6 / "
@@ -388,6 +455,11 @@ def lwm_128k_steps(seed, steps=64):
         "verify_int8_t6_gbps": round(float(np.mean(vb)) / (float(np.mean(ver)) * 1e-6) / 1e9, 1),
         "draft_int4_t1_us": round(draft_us, 3),
         "draft_int4_t1_gbps": round(draft_bytes / (draft_us * 1e-6) / 1e9, 1),
+        "verify_int8_by_T_us": {str(T): round(u, 3) for T, u in sweep_us.items()},
+        "verify_int8_by_T_gbps": {
+            str(T): round(algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv,
+                                            cache.n_q, cache.n_r, T, 8)
+                          / (u * 1e-6) / 1e9, 1) for T, u in sweep_us.items()},
     }
     del cache, kn, vn
     torch.cuda.empty_cache()
@@ -517,42 +589,75 @@ def main():
 
     events = []
 
+    def prime(i):
+        kq.kv_quant_append(caches[i % N_COPIES].c, k_new, v_new, T_VERIFY, sh)
+
     def step(i, timed):
-        c = caches[i % N_COPIES]
+        a = caches[i % N_COPIES]            # append + draft
+        b = caches[(i - LAG) % N_COPIES]    # verify + rollback (drafted LAG steps ago)
         if timed:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record(stream)
-        kq.kv_quant_append(c.c, k_new, v_new, T_VERIFY, sh)
+        kq.kv_quant_append(a.c, k_new, v_new, T_VERIFY, sh)
         if timed:
             e[1].record(stream)
-        kq.kv_attn_verify(c.c, q_draft, T_DRAFT, w.Hq, kq.KVQ_DRAFT4, sm,
+        kq.kv_attn_verify(a.c, q_draft, T_DRAFT, w.Hq, kq.KVQ_DRAFT4, sm,
                           out_d, None, ws, sh)
         if timed:
             e[2].record(stream)
-        kq.kv_attn_verify(c.c, q_verify, T_VERIFY, w.Hq, kq.KVQ_TARGET, sm,
+        kq.kv_attn_verify(b.c, q_verify, T_VERIFY, w.Hq, kq.KVQ_TARGET, sm,
                           out_v, None, ws, sh)
         if timed:
             e[3].record(stream)
             events.append(e)
-        kq.kv_rollback(c.c, T_VERIFY)
+        kq.kv_rollback(b.c, T_VERIFY)
 
-    for i in range(args.warmup):
+    # prime the pipeline: the LAG copies before step 0 hold their appended
+    # tokens (their drafts belong to the untimed prefix)
+    for i in range(-LAG, 0):
+        prime(i)
+    i = 0
+    for _ in range(args.warmup):
         step(i, False)
+        i += 1
     torch.cuda.synchronize()
     # 1) wall clock over K plain steps (no events in the stream)
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for _ in range(args.steps):
         step(i, False)
+        i += 1
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
     # 2) the same steps with per-kernel HIP events on the launch stream
-    for i in range(args.steps):
+    for _ in range(args.steps):
         step(i, True)
+        i += 1
     torch.cuda.synchronize()
+    # drain: verify and roll back the copies still holding appended tokens
+    for j in range(i - LAG, i):
+        kq.kv_rollback(caches[j % N_COPIES].c, T_VERIFY)
     app = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e3
     drf = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e3
     ver = np.array([e[2].elapsed_time(e[3]) for e in events]) * 1e3
     gpu_step = app + drf + ver
+    # 3) warm verify, for comparison only: right after the draft on the same
+    # copy, which has just read 37.5 MB of the verify's 70.9 MB
+    warm = []
+    for j in range(60):
+        c = caches[j % N_COPIES]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        kq.kv_quant_append(c.c, k_new, v_new, T_VERIFY, sh)
+        kq.kv_attn_verify(c.c, q_draft, T_DRAFT, w.Hq, kq.KVQ_DRAFT4, sm,
+                          out_d, None, ws, sh)
+        e[0].record(stream)
+        kq.kv_attn_verify(c.c, q_verify, T_VERIFY, w.Hq, kq.KVQ_TARGET, sm,
+                          out_v, None, ws, sh)
+        e[1].record(stream)
+        kq.kv_rollback(c.c, T_VERIFY)
+        if j >= 10:
+            warm.append(e)
+    torch.cuda.synchronize()
+    ver_warm = np.array([e[0].elapsed_time(e[1]) for e in warm]) * 1e3
 
     achieved = bytes_verify / (ver.mean() * 1e-6) / 1e9
     res = {
@@ -581,6 +686,7 @@ def main():
             "verify_int8_t7": round(float(np.median(ver)), 3),
             "verify_int8_t7_p10_p90": [round(float(np.percentile(ver, 10)), 3),
                                        round(float(np.percentile(ver, 90)), 3)],
+            "verify_int8_t7_warm": round(float(np.median(ver_warm)), 3),
             "gpu_step_events": round(float(gpu_step.mean()), 3),
             "prefill_32k": round(prefill_us, 3),
         },
@@ -610,7 +716,8 @@ def main():
                                              / ku["verify_int8_t7"], 3)
         comp["int4_vs_fp16_speedup"] = round(comp["fp16_decode_t1_us"]
                                              / ku["draft_int4_t1"], 3)
-        comp["specache_prefetch"] = specache_pipeline(args.seed)
+        comp["specache_prefetch"] = specache_pipeline(args.seed, "specache_2bit")
+        comp["specache_prefetch_1bit"] = specache_pipeline(args.seed, "specache_1bit")
         comp["lwm_128k"] = lwm_128k_steps(args.seed)
         comp["llama2_8k"] = llama2_8k(args.seed)
         res["comparators"] = comp
