@@ -193,6 +193,24 @@ int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq, int path,
                    float sm_scale, void* out, float* lse, void* ws,
                    size_t ws_bytes, void* stream);
 
+/* kv_attn_verify for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, semantics and results as kv_attn_verify
+ * without ws/ws_bytes: the split partials go to a static device scratch of
+ * 32 MiB that the library holds on every GPU it runs on until the process
+ * ends.  Nothing is allocated or freed, by the library or otherwise.
+ *   Limit: a call needs B*Hkv*rows_pad*(d+2)*4 bytes per split slot, rows_pad
+ *   = 16 when T*Hq/Hkv <= 16 else 32, and at least 2 slots in the scratch;
+ *   otherwise KVQ_EWORKSPACE (before any HIP call).  Within that, the split
+ *   count is the one kv_attn_verify plans whenever the scratch holds it.
+ *   Concurrency: every call on one GPU shares that GPU's scratch, so calls
+ *   that may overlap on one GPU (different streams, other threads) race;
+ *   order them.  The scratch keeps the last call's partials; a call needs
+ *   no initial contents. */
+int kv_attn_verify_noalloc(const kvq_cache* c, const void* q, int T, int Hq,
+                           int path, float sm_scale, void* out, float* lse,
+                           void* stream);
+
 /* Verify / draft attention with exact substitution for one query row
  * ([SC] Approach: the KV pairs the speculative token ranks highest are
  * fetched in full precision and used for the output token).  Same as

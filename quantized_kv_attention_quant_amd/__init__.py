@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
     L.kv_attn_workspace_bytes.argtypes = [P, i32, i32]
     L.kv_attn_workspace_bytes.restype = sz
     L.kv_attn_verify.argtypes = [P, vp, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+    L.kv_attn_verify_noalloc.argtypes = [P, vp, i32, i32, i32, f32, vp, vp, vp]
     L.kv_topk_workspace_bytes.argtypes = [P, i32, i32]
     L.kv_topk_workspace_bytes.restype = sz
     L.kv_topk.argtypes = [P, vp, i32, i32, i32, vp, vp, vp, sz, vp]
@@ -96,7 +97,8 @@ def lib() -> ctypes.CDLL:
     L.kv_last_error.argtypes = []
     L.kv_last_error.restype = ctypes.c_char_p
     for name in ("kv_cache_layout", "kv_quant_append", "kv_rollback",
-                 "kv_attn_verify", "kv_topk", "kv_dequant_gather",
+                 "kv_attn_verify", "kv_attn_verify_noalloc", "kv_topk",
+                 "kv_dequant_gather",
                  "kv_attn_verify_exact", "kv_fetch_rows"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -148,6 +150,13 @@ def kv_attn_verify(c: KvqCacheStruct, q, T: int, Hq: int, path, sm_scale: float,
         ctypes.byref(c), _ptr(q), T, Hq, _path(path), float(sm_scale),
         _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
         _stream(stream)))
+
+
+def kv_attn_verify_noalloc(c: KvqCacheStruct, q, T: int, Hq: int, path,
+                           sm_scale: float, out, lse, stream=None) -> None:
+    _check(lib().kv_attn_verify_noalloc(
+        ctypes.byref(c), _ptr(q), T, Hq, _path(path), float(sm_scale),
+        _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def kv_topk_workspace_bytes(c: KvqCacheStruct, Hq: int, k: int) -> int:

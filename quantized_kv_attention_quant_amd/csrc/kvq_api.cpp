@@ -178,10 +178,11 @@ KVQ_API size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq) {
 
 namespace {
 
-// Validation and argument set-up shared by the two attention entry points.
+// Validation and argument set-up shared by the attention entry points
+// (check_ws = false: the caller supplies the partial slots itself).
 int attn_setup(const kvq_cache* c, const void* q, int T, int Hq, int path,
                float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
-               kvq::AttnArgs& a) {
+               kvq::AttnArgs& a, bool check_ws = true) {
   int rc = check_cache(c);
   if (rc) return rc;
   if (!q || !out) return fail(KVQ_EINVAL, "q/out is NULL");
@@ -199,7 +200,7 @@ int attn_setup(const kvq_cache* c, const void* q, int T, int Hq, int path,
     return fail(KVQ_EINVAL, "the draft path reads 8-bit caches only");
   if (!std::isfinite(sm_scale)) return fail(KVQ_EINVAL, "sm_scale not finite");
   const size_t need = kv_attn_workspace_bytes(c, T, Hq);
-  if (!ws || ws_bytes < need)
+  if (check_ws && (!ws || ws_bytes < need))
     return fail(KVQ_EWORKSPACE, "workspace needs %zu bytes", need);
 
   a.g = kvq::geom_of(c);
@@ -236,6 +237,33 @@ KVQ_API int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq,
   if (rc) return rc;
   hipError_t e = kvq::launch_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_attn_verify launch");
+  return KVQ_OK;
+}
+
+KVQ_API int kv_attn_verify_noalloc(const kvq_cache* c, const void* q, int T,
+                                   int Hq, int path, float sm_scale, void* out,
+                                   float* lse, void* stream) {
+  kvq::AttnArgs a;
+  const int rc = attn_setup(c, q, T, Hq, path, sm_scale, out, lse, nullptr, 0, a,
+                            false);
+  if (rc) return rc;
+  // Partial slots per block that fit the static scratch (at most as many as
+  // the workspace entry point plans with, so the split count is the same
+  // whenever the scratch holds it).
+  const size_t slot = (size_t)c->B * c->Hkv * rows_pad_of(T, Hq, c->Hkv) *
+                      (c->d + 2) * sizeof(float);
+  const size_t fit = kvq::kScratchBytes / slot;
+  if (fit < 2)
+    return fail(KVQ_EWORKSPACE, "call needs %zu bytes per split slot and at "
+                "least 2 slots; the static scratch holds %zu bytes", slot,
+                kvq::kScratchBytes);
+  if ((size_t)a.s_alloc > fit) a.s_alloc = (int)fit;
+  void* scr = nullptr;
+  hipError_t e = kvq::attn_scratch(&scr);
+  if (e != hipSuccess) return hip_fail(e, "kv_attn_verify_noalloc scratch");
+  a.ws = (float*)scr;
+  e = kvq::launch_attn(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_attn_verify_noalloc launch");
   return KVQ_OK;
 }
 

@@ -42,6 +42,8 @@
 //     (m, l, o) per workgroup.  A second launch, one workgroup per (block,
 //     row), merges that row's partials by log-sum-exp (fp16 output, natural-
 //     log LSE); the kernel boundary makes the partials visible.
+#include <mutex>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -1286,6 +1288,12 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
 
 constexpr int kMaxDevices = 64;
 
+// Device scratch for kv_attn_verify_noalloc: the split partials of callers
+// that cannot allocate.  Every GPU the library runs on holds its own copy
+// until the process ends; host code uses the per-device address from
+// hipGetSymbolAddress, never the array's name (a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 // Workgroups of one instantiation resident per CU on `dev` (0 if unknown).
 template <int PATH, int D, int NG, int NRT, bool PAIR>
 int occupancy(int dev) {
@@ -1390,6 +1398,24 @@ int plan_splits(int64_t nb, int64_t slots, int64_t units, int streams, int cap) 
   if (best > by_units) best = by_units;
   if (best > cap) best = cap;
   return best < 1 ? 1 : (int)best;
+}
+
+hipError_t attn_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {              // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {

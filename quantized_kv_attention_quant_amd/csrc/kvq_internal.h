@@ -178,6 +178,11 @@ struct AttnArgs {
 // `units` units of work per block, nw waves per workgroup, at most cap.
 int plan_splits(int64_t nb, int64_t slots, int64_t units, int nw, int cap);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+// Static device scratch of kv_attn_verify_noalloc: kScratchBytes per GPU;
+// attn_scratch returns its address on the current device (looked up once
+// per device).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t attn_scratch(void** ptr);
 
 // On-demand reconstruction: see kv_dequant_gather.
 struct GatherArgs {

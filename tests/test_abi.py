@@ -28,6 +28,7 @@ def test_exports_match_header():
     names = _declared()
     assert names == {"kv_cache_layout", "kv_quant_append", "kv_rollback",
                      "kv_attn_workspace_bytes", "kv_attn_verify",
+                     "kv_attn_verify_noalloc",
                      "kv_topk_workspace_bytes", "kv_topk", "kv_dequant_gather",
                      "kv_attn_verify_exact", "kv_fetch_rows", "kv_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", kq.LIB_PATH],
