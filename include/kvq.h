@@ -166,7 +166,9 @@ int kv_rollback(kvq_cache* c, int m);
  * cache at any fill level: one fp32 partial (m, l, o for up to 32 rows) per
  * split of every block, for as many splits as the launcher may choose on a
  * device with up to 512 resident workgroup slots (it uses fewer on larger
- * devices), plus one spare slot per block for the substitution partial.
+ * devices), plus one spare slot per block for the substitution partial,
+ * then one bit per token slot (L_max/32 words per block) for the
+ * substitution's mask of fetched positions.
  * 0 if the shape is invalid.  Host only. */
 size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq);
 
@@ -222,9 +224,12 @@ int kv_attn_verify_noalloc(const kvq_cache* c, const void* q, int T, int Hq,
  *        (as kv_topk returns them); entries outside [0, n_q) are skipped
  *        (kv_topk's -1 padding).
  *   k_exact, v_exact: device fp16 [B][Hkv][n][d] (e.g. from kv_fetch_rows).
- * One more launch than kv_attn_verify: the substitution partial is computed
- * into a spare workspace slot and enters the same log-sum-exp merge, so a
- * fetched token's quantized term is removed and its exact term added.
+ * One more launch than kv_attn_verify, before the split pass: it writes a
+ * mask of the fetched positions and the partial of their exact terms (into
+ * a spare workspace slot); the split pass leaves the masked positions out
+ * of row t_exact, and the log-sum-exp merge adds the exact partial.  (No
+ * quantized term is subtracted, so the row stays accurate when a fetched
+ * token held most of its low-bit attention mass.)
  * Requires 0 <= n <= 256. */
 int kv_attn_verify_exact(const kvq_cache* c, const void* q, int T, int Hq,
                          int path, float sm_scale, int t_exact,

@@ -170,11 +170,23 @@ KVQ_API int kv_rollback(kvq_cache* c, int m) {
   return KVQ_OK;
 }
 
-KVQ_API size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq) {
-  if (check_shape(c) || T < 1 || Hq < 1 || Hq % c->Hkv) return 0;
+namespace {
+
+// Workspace: the split partials [B*Hkv][s_alloc][rows_pad][d + 2] floats,
+// then (exact substitution) one bit per quantized token of every block.
+size_t partial_bytes(const kvq_cache* c, int T, int Hq) {
   return (size_t)c->B * c->Hkv * s_alloc_of(c) * rows_pad_of(T, Hq, c->Hkv) *
          (c->d + 2) * sizeof(float);
 }
+
+}  // namespace
+
+KVQ_API size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq) {
+  if (check_shape(c) || T < 1 || Hq < 1 || Hq % c->Hkv) return 0;
+  return partial_bytes(c, T, Hq) +
+         (size_t)c->B * c->Hkv * (c->L_max / 32) * sizeof(uint32_t);
+}
+
 
 namespace {
 
@@ -224,6 +236,7 @@ int attn_setup(const kvq_cache* c, const void* q, int T, int Hq, int path,
   a.t_exact = 0;
   a.idx_exact = nullptr;
   a.k_exact = a.v_exact = nullptr;
+  a.xmask = nullptr;
   return KVQ_OK;
 }
 
@@ -285,6 +298,7 @@ KVQ_API int kv_attn_verify_exact(const kvq_cache* c, const void* q, int T, int H
   a.idx_exact = idx;
   a.k_exact = (const __half*)k_exact;
   a.v_exact = (const __half*)v_exact;
+  a.xmask = (unsigned*)((char*)ws + partial_bytes(c, T, Hq));
   hipError_t e = kvq::launch_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_attn_verify_exact launch");
   return KVQ_OK;

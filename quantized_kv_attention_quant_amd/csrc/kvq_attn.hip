@@ -377,72 +377,34 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
 }
 
 // Exact substitution, one workgroup per (group of up to HB GQA heads, kv
-// head, batch): the partial that turns query row t_exact * gs + hl's
-// attention over the quantized cache into attention where the positions
-// idx_exact read the exact fp16 K/V (SpeCache page, Approach: the fetched
-// pairs are used in full precision for the output token).  With logits in
-// the log2 domain, sq_j from the dequantized key and se_j from the exact one:
-//   l = sum_j (2^(se_j - m) - 2^(sq_j - m)),
-//   o = sum_j (2^(se_j - m) v_j - 2^(sq_j - m) v^_j),   m = max_j (sq_j, se_j)
-// written to the spare partial slot S of the block; the log-sum-exp merge of
-// the S + 1 partials then removes each fetched token's quantized term and
-// adds its exact one.  The other query rows of those heads get an empty
-// partial (m = -inf, l = 0, o = 0).  Positions outside [0, n_q) are skipped.
-// 512 threads, two workgroups per CU (so a batched call's workgroups run in
-// one round): each wave takes fetched tokens w, w + 8, ... with its lanes
-// over the channels and issues all K and V loads of UT tokens together (the
-// positions are scattered, so each round of loads is long); the heads of
-// the kv group share the loaded rows.  Each wave keeps (m, l, o) per head
-// with the usual rescaling, and the 8 wave states meet in LDS by
-// log-sum-exp.  Skipped entries read stand-in position 0 and are never
-// folded in.  The code width W is a template parameter and every division
-// in the element addressing is a shift (Gv divides d, a power of two) except
-// one 32-bit divide per token for its key group: there is no integer divide
-// instruction, and per-element software divides made the kernel ALU-bound.
-
-// Dequantized key and value element (channel c) of quantized token pos of
-// block blk, from the documented layouts: key group grp = pos / G, value
-// tile pos / 32.
-template <int W, int D>
-__device__ inline float2 exact_kv_deq(const AttnArgs& a, int64_t blk, int pos,
-                                      int grp, int c, int gv_sh, bool draft) {
-  const CacheGeom& g = a.g;
-  constexpr bool TWO = W == 4;                   // 8-bit codes: two planes
-  constexpr unsigned MASK = (1u << W) - 1u;
-  constexpr int PB = 8 / W;                      // key codes per byte
-  // key: byte c / PB of the token's plane row, bits W * (c % PB)
-  const int64_t row = blk * g.k_block_bytes + (int64_t)pos * g.k_row_bytes + c / PB;
-  const int ksh = W * (c % PB);
-  const unsigned khi = ((unsigned)a.p.k_hi[row] >> ksh) & MASK;
-  const unsigned klo = TWO ? ((unsigned)a.p.k_lo[row] >> ksh) & MASK : 0u;
-  const __half2 ksz = a.p.k_sz[blk * g.ksz_block + (int64_t)grp * D + c];
-  // value: token j of its 32-token tile, dword (16 jg + r) (D W / 64) + m / per
-  // of the tile, bits 16 jh + W (4 (m % per) + ji)
-  constexpr int PER = 4 / W;
-  const int j = pos % kTile, jg = (j % 16) / 4, ji = j % 4, jh = j / 16;
-  const int r = c % 16, m = c / 16;
-  const int dw = (16 * jg + r) * (D * W / 64) + m / PER;
-  const int vsh = 16 * jh + W * (4 * (m % PER) + ji);
-  const int64_t tile = blk * g.v_block_bytes + (int64_t)(pos / kTile) * g.v_tile_bytes;
-  const unsigned vhi = (((const uint32_t*)(a.p.v_hi + tile))[dw] >> vsh) & MASK;
-  const unsigned vlo = TWO ? (((const uint32_t*)(a.p.v_lo + tile))[dw] >> vsh) & MASK : 0u;
-  // the value group's (s, z): halves [part][g][i][group][h] of the tile
-  const int ngv = D >> gv_sh, gg = c >> gv_sh;
-  const __half* t = (const __half*)(a.p.v_sz + blk * g.vsz_block +
-                                    (int64_t)(pos / kTile) * g.vsz_tile);
-  const int so = (jg * 4 + ji) * ngv * 2 + gg * 2 + jh;
-  const int zo = ((4 + jg) * 4 + ji) * ngv * 2 + gg * 2 + jh;
-  const float kc = code_value(khi, klo, TWO, draft);
-  const float vc = code_value(vhi, vlo, TWO, draft);
-  return make_float2(__high2float(ksz) + kc * __low2float(ksz),
-                     __half2float(t[zo]) + vc * __half2float(t[so]));
-}
-
-template <int D, int RP, int W>
+// head, batch) (SpeCache page, Approach: the fetched pairs are used in full
+// precision for the output token).  It runs before the split pass and
+// writes two things:
+//   * the block's mask of fetched positions, one bit per quantized token
+//     (word t covers tile t), which the split pass reads to leave those
+//     positions out of query row t_exact's attention;
+//   * the partial of the fetched tokens' exact terms for row t_exact of each
+//     head, with logits se_j in the log2 domain from the exact keys:
+//       m = max_j se_j,  l = sum_j 2^(se_j - m),  o = sum_j 2^(se_j - m) v_j,
+//     into the spare partial slot S of the block, so the log-sum-exp merge
+//     of the S + 1 partials gives the row its attention with the fetched
+//     positions reading the exact fp16 K/V.  The other query rows of those
+//     heads get an empty partial (m = -inf, l = 0, o = 0).
+// Positions outside [0, n_q) are skipped.  Leaving the positions out of the
+// split pass, instead of subtracting their quantized terms afterwards, keeps
+// the result accurate when a fetched token carried most of the quantized
+// attention mass but little of the exact one (no cancellation).
+// 512 threads, two workgroups per CU: each wave takes fetched tokens w,
+// w + 8, ... with its lanes over the channels and loads the fp16 rows of UT
+// tokens together (the positions are scattered); the heads of the kv group
+// share the loaded rows.  Each wave keeps (m, l, o) per head with the usual
+// rescaling, and the 8 wave states meet in LDS by log-sum-exp.  Skipped
+// entries read stand-in row 0 and are never folded in.
+template <int D, int RP>
 __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
   constexpr int NT = 512, HB = 4;                // heads per workgroup
   constexpr int NWV = NT / kWave, CPL = D / kWave;
-  constexpr int UT = CPL == 1 ? 4 : 2;          // tokens a wave loads together
+  constexpr int UT = 4;                          // tokens a wave loads together
   __shared__ float s_q[HB][D];
   __shared__ int s_idx[kMaxExact];
   __shared__ float s_o[NWV][HB][D], s_m[NWV][HB], s_l[NWV][HB];
@@ -452,13 +414,23 @@ __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = a.n_exact;
-  const bool draft = a.path == KVQ_DRAFT4;
   const int64_t pstride = (int64_t)RP * (D + 2);
   float* po = a.ws + (blk * a.s_alloc + a.S) * pstride;
   const __half* ke = a.k_exact + blk * n * D;
   const __half* ve = a.v_exact + blk * n * D;
-  const int gv_sh = __builtin_ctz((unsigned)g.Gv);   // Gv is a power of two
 
+  for (int i = tid; i < n; i += NT) s_idx[i] = a.idx_exact[blk * n + i];
+  // the block's mask of fetched positions (one workgroup per block writes it)
+  if (blockIdx.x == 0) {
+    unsigned* mw = a.xmask + blk * (g.L_max / kTile);
+    const int nw = (int)(a.n_q / kTile);
+    for (int w = tid; w < nw; w += NT) mw[w] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const int p = s_idx[i];
+      if (p >= 0 && p < a.n_q) atomicOr(mw + (p >> 5), 1u << (p & 31));
+    }
+  }
   // empty partials for these heads' other query rows
   for (int t = 0; t < a.T; ++t) {
     if (t == a.t_exact) continue;
@@ -474,10 +446,9 @@ __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
   for (int e = tid; e < HB * D; e += NT) {
     const int hh = e / D, c = e % D;
     s_q[hh][c] = hh < nh ? __half2float(a.q[(((int64_t)b * a.T + a.t_exact) * a.Hq +
-                                             kvh * a.gs + hl0 + hh) * D + c])
+                                             kvh * a.gs + hl0 + hh) * D + c]) * a.c0
                          : 0.f;
   }
-  for (int i = tid; i < n; i += NT) s_idx[i] = a.idx_exact[blk * n + i];
   __syncthreads();
 
   float m[HB], l[HB], o[HB][CPL];
@@ -489,55 +460,41 @@ __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
     for (int k = 0; k < CPL; ++k) o[hh][k] = 0.f;
   }
   for (int i0 = wave; i0 < n; i0 += NWV * UT) {
-    // every load of the UT tokens first
-    float kq[UT][CPL], kx[UT][CPL], vq[UT][CPL], vx[UT][CPL];
+    float kx[UT][CPL], vx[UT][CPL];
     bool ok[UT];
 #pragma unroll
-    for (int u = 0; u < UT; ++u) {
+    for (int u = 0; u < UT; ++u) {               // every load of the UT tokens first
       const int i = i0 + u * NWV;
-      const int64_t p = i < n ? s_idx[i] : -1;
+      const int p = i < n ? s_idx[i] : -1;
       ok[u] = p >= 0 && p < a.n_q;
-      const int ps = ok[u] ? (int)p : 0;       // stand-in: never folded in
-      const int grp = (int)((unsigned)ps / (unsigned)g.G);   // n_q < 2^24
-      const int64_t is = i < n ? i : 0;
+      const int64_t is = ok[u] ? i : 0;          // stand-in: never folded in
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
         const int c = lane + kWave * k;
-        const float2 kv = exact_kv_deq<W, D>(a, blk, ps, grp, c, gv_sh, draft);
-        kq[u][k] = kv.x;
         kx[u][k] = __half2float(ke[is * D + c]);
-        vq[u][k] = kv.y;
         vx[u][k] = __half2float(ve[is * D + c]);
       }
     }
 #pragma unroll
     for (int u = 0; u < UT; ++u) {
-      float dq[HB], de[HB];
+      float de[HB];
 #pragma unroll
       for (int hh = 0; hh < HB; ++hh) {
-        dq[hh] = de[hh] = 0.f;
+        de[hh] = 0.f;
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          dq[hh] += s_q[hh][lane + kWave * k] * kq[u][k];
-          de[hh] += s_q[hh][lane + kWave * k] * kx[u][k];
-        }
+        for (int k = 0; k < CPL; ++k) de[hh] += s_q[hh][lane + kWave * k] * kx[u][k];
 #pragma unroll
-        for (int sh = 1; sh < kWave; sh <<= 1) {
-          dq[hh] += __shfl_xor(dq[hh], sh);
-          de[hh] += __shfl_xor(de[hh], sh);
-        }
+        for (int sh = 1; sh < kWave; sh <<= 1) de[hh] += __shfl_xor(de[hh], sh);
       }
       if (ok[u]) {                              // wave-uniform: one token per wave
 #pragma unroll
         for (int hh = 0; hh < HB; ++hh) {
-          const float sq = dq[hh] * a.c0, se = de[hh] * a.c0;
-          const float mn = fmaxf(m[hh], fmaxf(sq, se));
+          const float mn = fmaxf(m[hh], de[hh]);
           const float alpha = fast_exp2(m[hh] - mn);   // 0 while m = -inf
-          const float we = fast_exp2(se - mn), wq = fast_exp2(sq - mn);
-          l[hh] = l[hh] * alpha + (we - wq);
+          const float we = fast_exp2(de[hh] - mn);
+          l[hh] = l[hh] * alpha + we;
 #pragma unroll
-          for (int k = 0; k < CPL; ++k)
-            o[hh][k] = o[hh][k] * alpha + (we * vx[u][k] - wq * vq[u][k]);
+          for (int k = 0; k < CPL; ++k) o[hh][k] = o[hh][k] * alpha + we * vx[u][k];
           m[hh] = mn;
         }
       }
@@ -580,7 +537,10 @@ __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
 //   s_q     fp16 [RP][D]      this block's query rows (zero past `rows`)
 // After the unit loop the same bytes hold the stream-merge slabs
 //   slab float [NS][RP][D+4], ml float [NS][2][RP].
-template <int PATH, int D, int NG, int NRT, bool PAIR>
+// XM: exact substitution (a.xmask set): query row t_exact leaves the
+// fetched positions out (a separate instantiation, so the plain path keeps
+// its registers).
+template <int PATH, int D, int NG, int NRT, bool PAIR, bool XM>
 __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     attn_kernel(const AttnArgs a) {
   using C = Cfg<PATH, D, NG, NRT, PAIR>;
@@ -687,8 +647,22 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
                              C::NI_TILE - chunks_of(C::KSZB)};
   // parts: 1 = keys and scales, 2 = values (with DIRECTK the values too come
   // straight to the registers, lane l holding its 32 bytes of each plane)
+  // XM: the fetched-position mask words of the unit being fetched (loaded
+  // before its chunks, so waiting for them never waits for the unit) and of
+  // the unit being computed (taken at its commit)
+  unsigned xwp[C::TPU], xwc[C::TPU];
+#pragma unroll
+  for (int j = 0; j < C::TPU; ++j) xwp[j] = xwc[j] = 0u;
+  const unsigned* xm_blk = XM ? a.xmask + blk * (g.L_max / kTile) : nullptr;
   auto fetch_quant = [&](int u, int parts) __attribute__((always_inline)) {
     const int t0 = (u - nres) * C::TPU;
+    if constexpr (XM) {
+      if (parts & 1) {
+#pragma unroll
+        for (int j = 0; j < C::TPU; ++j)
+          xwp[j] = xm_blk[t0 + j < nqt ? t0 + j : nqt - 1];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < C::TPU; ++j) {
       int t = t0 + j < nqt ? t0 + j : nqt - 1;
@@ -739,6 +713,10 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
       for (int i = 0; i < C::NIR; ++i)
         *(u4v*)(stages + 1024 * i + ((i & 1) ? pk1 : pk)) = stg[i];
     } else {
+      if constexpr (XM) {
+#pragma unroll
+        for (int j = 0; j < C::TPU; ++j) xwc[j] = __builtin_amdgcn_readfirstlane(xwp[j]);
+      }
 #pragma unroll
       for (int j = 0; j < C::TPU; ++j) {
         constexpr int bytes[6] = {C::PL, C::TWO ? C::PL : 0, C::PL, C::TWO ? C::PL : 0,
@@ -805,6 +783,8 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     for (int ks = 0; ks < KS; ++ks) bqh[rt][ks] = bql[rt][ks] = u4v{0u, 0u, 0u, 0u};
   }
   int cur_grp = -2;                    // -1: ring operands, >= 0: key group
+  // exact substitution: rows of query token t_exact (one per GQA head)
+  const int xlo = a.t_exact * a.gs, xhi = xlo + a.gs;
   const DecK dk = dec_consts();
   const float c0 = a.c0;
   // channels this lane multiplies in key-group operands: (cA(ks) + j,
@@ -979,7 +959,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   };
 
   // ---- one quantized 32-token tile from LDS
-  auto quant_tile = [&](const unsigned char* tb, int t, bool may_build, int u, bool next)
+  auto quant_tile = [&](const unsigned char* tb, int t, int j, bool may_build, int u, bool next)
       __attribute__((always_inline)) {
     u4v ak[2][KS];
 #pragma unroll
@@ -1024,6 +1004,23 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     }
     f4v sc[2][NRT];
     scores(sc, ak);
+    if constexpr (XM) {          // row t_exact leaves fetched positions out
+      const unsigned xw = xwc[j];
+      if (xw) {                  // wave-uniform: most tiles have none
+        const unsigned m4 = xw >> (4 * gq);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          const int row = row_of(rt);
+          if (row >= xlo && row < xhi) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if ((m4 >> (16 * st + i)) & 1u) sc[st][rt][i] = -INFINITY;
+          }
+        }
+      }
+    }
     // value scale pairs (tokens 4gq+i, 16+4gq+i; [i][group]) and zero pairs
     unsigned sz[8 * NG];
     lds_read<4 * NG>(tb + C::O_VSZ + 16 * NG * gq, sz);
@@ -1194,7 +1191,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     const int t0 = (u - nres) * C::TPU;
 #pragma unroll
     for (int j = 0; j < C::TPU; ++j)
-      if (t0 + j < nqt) quant_tile(stages + j * C::TILE, t0 + j, may_build, u, next);
+      if (t0 + j < nqt) quant_tile(stages + j * C::TILE, t0 + j, j, may_build, u, next);
   };
   auto in_group = [&](int u) __attribute__((always_inline)) {
     const int t0 = (u - nres) * C::TPU;
@@ -1295,26 +1292,26 @@ constexpr int kMaxDevices = 64;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 // Workgroups of one instantiation resident per CU on `dev` (0 if unknown).
-template <int PATH, int D, int NG, int NRT, bool PAIR>
+template <int PATH, int D, int NG, int NRT, bool PAIR, bool XM>
 int occupancy(int dev) {
   using C = Cfg<PATH, D, NG, NRT, PAIR>;
   static int cache[kMaxDevices];   // 0 = not queried yet
   if (dev < 0 || dev >= kMaxDevices) return 0;
   if (cache[dev] == 0) {
     hipError_t e = hipFuncSetAttribute(
-        (const void*)attn_kernel<PATH, D, NG, NRT, PAIR>,
+        (const void*)attn_kernel<PATH, D, NG, NRT, PAIR, XM>,
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return 0;
     int n = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &n, (const void*)attn_kernel<PATH, D, NG, NRT, PAIR>, C::NW * kWave, C::LDS);
+        &n, (const void*)attn_kernel<PATH, D, NG, NRT, PAIR, XM>, C::NW * kWave, C::LDS);
     if (e != hipSuccess || n < 1) return 0;
     cache[dev] = n;
   }
   return cache[dev];
 }
 
-template <int PATH, int D, int NG, int NRT, bool PAIR>
+template <int PATH, int D, int NG, int NRT, bool PAIR, bool XM>
 hipError_t go(AttnArgs a, hipStream_t s) {
   using C = Cfg<PATH, D, NG, NRT, PAIR>;
   int dev = 0, cus = 0;
@@ -1322,7 +1319,7 @@ hipError_t go(AttnArgs a, hipStream_t s) {
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const int occ = occupancy<PATH, D, NG, NRT, PAIR>(dev);
+  const int occ = occupancy<PATH, D, NG, NRT, PAIR, XM>(dev);
   if (occ < 1) return hipErrorInvalidConfiguration;
   const int64_t nb = (int64_t)a.g.B * a.g.Hkv;
   const int64_t units = 2 * cdiv(a.n_r, kTile) + cdiv(a.n_q / kTile, C::TPU);
@@ -1333,25 +1330,22 @@ hipError_t go(AttnArgs a, hipStream_t s) {
   a.grp_shift = -1;
   for (int k = 0; k < 31; ++k)
     if (tpg == 1 << k) a.grp_shift = k;
+  // exact substitution first: it writes the mask of fetched positions the
+  // split pass reads, and the exact-term partial into the spare slot S
+  if (a.n_exact >= 0) {
+    const dim3 xg((unsigned)cdiv(a.gs, 4), (unsigned)a.g.Hkv, (unsigned)a.g.B);
+    hipLaunchKernelGGL((exact_kernel<D, C::RP>), xg, dim3(512), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // grid: splits x kv heads x batch; consecutive workgroups are consecutive
   // splits of one block
-  hipLaunchKernelGGL((attn_kernel<PATH, D, NG, NRT, PAIR>),
+  hipLaunchKernelGGL((attn_kernel<PATH, D, NG, NRT, PAIR, XM>),
                      dim3((unsigned)a.S, (unsigned)a.g.Hkv, (unsigned)a.g.B),
                      dim3(C::NW * kWave), C::LDS, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.n_exact >= 0) {
-    const dim3 xg((unsigned)cdiv(a.gs, 4), (unsigned)a.g.Hkv, (unsigned)a.g.B);
-    if (a.g.w == 4)
-      hipLaunchKernelGGL((exact_kernel<D, C::RP, 4>), xg, dim3(512), 0, s, a);
-    else if (a.g.w == 2)
-      hipLaunchKernelGGL((exact_kernel<D, C::RP, 2>), xg, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((exact_kernel<D, C::RP, 1>), xg, dim3(512), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    ++a.S;                       // the merge reads the substitution partial too
-  }
+  if (a.n_exact >= 0) ++a.S;     // the merge reads the substitution partial too
   hipLaunchKernelGGL((merge_kernel<D, C::RP>),
                      dim3((unsigned)a.rows, (unsigned)a.g.Hkv, (unsigned)a.g.B),
                      dim3(256), 0, s, a);
@@ -1361,9 +1355,12 @@ hipError_t go(AttnArgs a, hipStream_t s) {
 template <int PATH, int D, int NRT, bool PAIR>
 hipError_t by_ng(const AttnArgs& a, hipStream_t s) {
   switch (a.g.d / a.g.Gv) {
-    case 1: return go<PATH, D, 1, NRT, PAIR>(a, s);
-    case 2: return go<PATH, D, 2, NRT, PAIR>(a, s);
-    case 4: return go<PATH, D, 4, NRT, PAIR>(a, s);
+    case 1: return a.xmask ? go<PATH, D, 1, NRT, PAIR, true>(a, s)
+                           : go<PATH, D, 1, NRT, PAIR, false>(a, s);
+    case 2: return a.xmask ? go<PATH, D, 2, NRT, PAIR, true>(a, s)
+                           : go<PATH, D, 2, NRT, PAIR, false>(a, s);
+    case 4: return a.xmask ? go<PATH, D, 4, NRT, PAIR, true>(a, s)
+                           : go<PATH, D, 4, NRT, PAIR, false>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -173,6 +173,7 @@ struct AttnArgs {
   const int32_t* idx_exact; // [B][Hkv][n_exact] quantized positions (-1: skip)
   const __half* k_exact;    // [B][Hkv][n_exact][d]
   const __half* v_exact;    // [B][Hkv][n_exact][d]
+  unsigned* xmask;          // [B*Hkv][L_max/32] fetched-position bits, or NULL
 };
 // Splits per block for nb blocks on `slots` resident workgroup slots, with
 // `units` units of work per block, nw waves per workgroup, at most cap.

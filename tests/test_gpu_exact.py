@@ -197,3 +197,64 @@ def test_verify_exact_without_substitutions_equals_verify():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), n
         assert torch.equal(lse, ref_lse), n
+
+
+@pytest.mark.parametrize("bits", [1, 2])
+def test_verify_exact_dominant_fetched_token(bits):
+    """A fetched token that carries almost all of the low-bit attention mass
+    of the substituted row while its exact logit is small: the query is
+    aligned with that token's dequantized key, whose exact key sits near the
+    middle of every group's range.  The substituted row must then follow
+    the exact softmax, where that token is negligible (within 2e-3 of the
+    oracle: no cancellation between its quantized and exact terms)."""
+    w = W(f"dominant_{bits}bit", 1, 8, 2, 128, 1000, 32, 32, 32, bits, "normal")
+    T, t_exact, jstar = 2, 0, 333
+    top = 25.0 if bits == 1 else 45.0        # jstar's low-bit logit
+    say(f"[gpu] exact substitution, dominant fetched token, {bits}-bit")
+    K, V = host_tokens(w, 0)
+    K[:, jstar] = np.float16(0.1)            # mid-range: its low-bit codes round up
+    shape = shape_for(w, max_append=64)
+    cache = kq.QuantKVCache(shape)
+    rep = ocache.Replay(w.B, w.Hkv, w.d, w.G, w.Gv, w.bits, w.R)
+    cache.append(to_dev(K), to_dev(V))
+    rep.append(K, V)
+    assert jstar < rep.n_q
+    sm = w.d ** -0.5
+    gs = w.Hq // w.Hkv
+    q16 = synth.queries(w, 5, T)
+    for h in range(w.Hkv):                   # row t_exact: along k^(jstar)
+        kh = attention.block_kv(rep.kq[0, h], rep.ks[0, h], rep.kz[0, h],
+                                rep.vq[0, h], rep.vs[0, h], rep.vz[0, h],
+                                rep.rk[0, h], rep.rv[0, h], w.G, w.Gv,
+                                "target")[0][jstar]
+        q16[0, t_exact, h * gs:(h + 1) * gs] = (
+            top / (sm * np.linalg.norm(kh)) * kh / np.linalg.norm(kh)).astype(np.float16)
+    rng = np.random.default_rng(3)
+    n = 12
+    idx = np.empty((w.B, w.Hkv, n), np.int32)
+    for h in range(w.Hkv):
+        others = rng.choice([p for p in range(rep.n_q) if p != jstar], n - 1,
+                            replace=False)
+        idx[0, h] = np.concatenate([[jstar], others])
+    kxo = np.stack([[K[0, idx[0, h], h] for h in range(w.Hkv)]])
+    vxo = np.stack([[V[0, idx[0, h], h] for h in range(w.Hkv)]])
+    out, lse = cache.verify_exact(to_dev(q16), to_dev(idx), to_dev(kxo),
+                                  to_dev(vxo), t_exact=t_exact, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = attention.attend_exact(rep, q16, "target", sm, idx, kxo, vxo,
+                                          t_exact)
+    base, _ = attention.attend(rep, q16, "target", sm)
+    # the case is what it claims: the quantized softmax of the row puts
+    # almost all of its mass on jstar, the exact one almost none
+    Kq, _ = attention.block_kv(rep.kq[0, 0], rep.ks[0, 0], rep.kz[0, 0],
+                               rep.vq[0, 0], rep.vs[0, 0], rep.vz[0, 0],
+                               rep.rk[0, 0], rep.rv[0, 0], w.G, w.Gv, "target")
+    lq = sm * Kq[:rep.n_q] @ q16[0, t_exact, 0].astype(np.float64)
+    assert lq[jstar] - np.log(np.exp(lq - lq.max()).sum()) - lq.max() > -0.01
+    le = sm * K[0, :rep.n_q, 0].astype(np.float64) @ q16[0, t_exact, 0].astype(np.float64)
+    assert le[jstar] < le.max() - 3
+    assert np.abs(ref[0, t_exact] - base[0, t_exact]).max() > 0.1
+    rel = assert_attn_close(out.cpu().numpy(), ref, f"dominant {bits}-bit")
+    lerr = np.abs(lse.cpu().numpy() - ref_lse)
+    say(f"    rel err {rel:.2e}; lse err {lerr.max():.2e}")
+    assert lerr.max() <= 1e-3
