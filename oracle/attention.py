@@ -33,7 +33,20 @@ import numpy as np
 
 from . import quant
 
-__all__ = ["block_kv", "attend_block", "attend", "attend_exact"]
+__all__ = ["block_kv", "attend_block", "attend", "attend_exact",
+           "max_value_scale", "VALUE_SCALE_LIMIT"]
+
+# Domain of the inputs (a reading, with finiteness): every value group's
+# scale is at most 63.  The library's attention multiplies fp16
+# probabilities scaled to at most 2^10 by the value scale in fp16, which
+# stays finite up to 63; the oracle itself has no such limit.
+VALUE_SCALE_LIMIT = 63.0
+
+
+def max_value_scale(rep) -> float:
+    """Largest value-group scale in an ``oracle.cache.Replay`` (0 when
+    nothing is quantized), to check inputs against VALUE_SCALE_LIMIT."""
+    return float(rep.vs.max()) if rep.vs.size else 0.0
 
 
 def block_kv(kq, ks, kz, vq, vs, vz, rk, rv, G, Gv, path):

@@ -123,3 +123,18 @@ def lse_tolerance(rep, q16, path, sm_scale):
             bound = sm_scale * (2.0 ** -21 * mag + 16 * 2.0 ** -24 * top * acc)
             tol[b, h * gs:(h + 1) * gs] = (2 * bound).T
     return tol + 2e-6
+
+
+def assert_block_bytes(cache: kq.QuantKVCache, b: int, h: int, rep,
+                       rb: int = 0, rh: int = 0, what: str = ""):
+    """Block (b, h) of the device cache equals block (rb, rh) of an oracle
+    replay: codes bit for bit, scales and zeros as fp16 values, residual
+    tokens bit for bit."""
+    got = read_block(cache, b, h)
+    for name in ("kq", "vq"):
+        assert np.array_equal(got[name], getattr(rep, name)[rb, rh]), (what, name)
+    for name in ("rk", "rv"):
+        assert np.array_equal(got[name].view(np.uint16),
+                              getattr(rep, name)[rb, rh].view(np.uint16)), (what, name)
+    for name in ("ks", "kz", "vs", "vz"):
+        assert np.array_equal(got[name], getattr(rep, name)[rb, rh]), (what, name)

@@ -17,7 +17,8 @@ import torch
 import kvq_synth as synth
 import quantized_kv_attention_quant_amd as kq
 from oracle import attention, cache as ocache, topk as otopk
-from kvq_testlib import assert_attn_close, lse_tolerance, say, shape_for
+from kvq_testlib import (assert_attn_close, assert_block_bytes, lse_tolerance,
+                         say, shape_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +44,11 @@ def device_tokens(w, seed, L, sampled):
 
 class Mirror:
     """Oracle replays of the sampled blocks, fed the same appends."""
+
+    def check_bytes(self, cache, label):
+        """The sampled blocks' quantized store and residual, byte for byte."""
+        for (b, h), rep in self.rep.items():
+            assert_block_bytes(cache, b, h, rep, 0, 0, f"{label} ({b},{h})")
 
     def __init__(self, w, host):
         self.w, self.host = w, host
@@ -111,6 +117,7 @@ def test_llama3_32k_bench_step():
     qd, qv = synth.queries(w, 0, 1), synth.queries(w, 1, 7)
     cache.append(K[:, L0:].contiguous(), V[:, L0:].contiguous())
     mirror.append(L0, w.L)
+    mirror.check_bytes(cache, "32K store")
     d0 = check_attention(cache, mirror, qd, "draft4", "draft")
     t0 = check_attention(cache, mirror, qv, "target", "verify")
     cache.rollback(7)
@@ -169,6 +176,7 @@ def test_lwm_128k_append6_rollback2():
             mirror.rollback(2)
             p -= 2
     assert p == w.L
+    mirror.check_bytes(cache, "128K store")
 
 
 @pytest.mark.parametrize("name", ["specache_1bit", "specache_2bit"])
@@ -183,6 +191,7 @@ def test_specache_batched_attention_and_topk(name):
     mirror.append(0, w.L - 2)
     cache.append(K[:, w.L - 2:].contiguous(), V[:, w.L - 2:].contiguous())
     mirror.append(w.L - 2, w.L)
+    mirror.check_bytes(cache, f"{name} store")
     q16 = synth.queries(w, 3, 2)
     check_attention(cache, mirror, q16, "target", "T=2")
     qs16 = np.ascontiguousarray(q16[:, 1])          # the speculative token
