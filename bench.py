@@ -341,6 +341,60 @@ def specache_pipeline(seed, name="specache_2bit", steps=30):
     us = {n: float(np.median([a.elapsed_time(b) for a, b in v])) * 1e3
           for n, v in ts.items()}
     fetch_bytes = 2 * w.B * w.Hkv * k * w.d * 2
+
+    # A contiguous host -> device copy of as many bytes as the fetch moves
+    # (the page's sparse-vs-full transfer comparison).
+    flat = mirror.k.view(-1)[:fetch_bytes // 2]
+    dst = torch.empty(fetch_bytes // 2, dtype=torch.float16, device=dev)
+    cts = []
+    for i in range(steps + 3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(flat, non_blocking=True)
+        e1.record(stream)
+        if i >= 3:
+            cts.append((e0, e1))
+    torch.cuda.synchronize()
+    contig_us = float(np.median([a.elapsed_time(b) for a, b in cts])) * 1e3
+
+    # Pipelined steps: step i's output token attends with the rows fetched
+    # for step i-1's top-k; step i's top-k then starts the next fetch on a
+    # second stream (default priority), which runs while step i+1's mask and
+    # split pass do: only the exact-term kernel waits for it (rows_ready).
+    copy = torch.cuda.Stream(device=dev)
+    idxs = [torch.empty_like(idx) for _ in range(2)]
+    kxs = [torch.empty_like(kx) for _ in range(2)]
+    vxs = [torch.empty_like(vx) for _ in range(2)]
+    e_topk = [torch.cuda.Event() for _ in range(2)]
+    e_fetch = [torch.cuda.Event() for _ in range(2)]
+
+    def start_fetch(cur):
+        cache.topk(q_spec, k, idx=idxs[cur], ws=tws)
+        e_topk[cur].record(stream)
+        copy.wait_event(e_topk[cur])
+        mirror.fetch(cache, idxs[cur], kxs[cur], vxs[cur], stream=copy)
+        e_fetch[cur].record(copy)
+
+    def pipe_step(i):
+        prev = (i - 1) % 2
+        cache.verify_exact(q, idxs[prev], kxs[prev], vxs[prev], t_exact=0,
+                           out=out, ws=aws, rows_ready=e_fetch[prev])
+        start_fetch(i % 2)
+
+    start_fetch(1)                       # the step before the first
+    for i in range(3):
+        pipe_step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(3, 3 + steps):
+        pipe_step(i)
+    stream.wait_event(e_fetch[(2 + steps) % 2])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    overlapped_us = e0.elapsed_time(e1) * 1e3 / steps
     verify_bytes = w.B * algorithmic_bytes(w.Hkv, w.Hq, w.d, w.G, w.Gv,
                                            cache.n_q, cache.n_r, T, w.bits)
     res = {
@@ -353,6 +407,9 @@ def specache_pipeline(seed, name="specache_2bit", steps=30):
         "verify_us": round(us["verify"], 3),
         "verify_gbps": round(verify_bytes / (us["verify"] * 1e-6) / 1e9, 1),
         "pipeline_us": round(us["topk"] + us["fetch"] + us["verify_exact"], 3),
+        "pipeline_overlapped_us": round(overlapped_us, 3),
+        "contiguous_copy_us": round(contig_us, 3),
+        "sparse_vs_contiguous_time": round(us["fetch"] / contig_us, 2),
     }
     del cache, mirror
     torch.cuda.empty_cache()

@@ -224,18 +224,24 @@ int kv_attn_verify_noalloc(const kvq_cache* c, const void* q, int T, int Hq,
  *        (as kv_topk returns them); entries outside [0, n_q) are skipped
  *        (kv_topk's -1 padding).
  *   k_exact, v_exact: device fp16 [B][Hkv][n][d] (e.g. from kv_fetch_rows).
- * One more launch than kv_attn_verify, before the split pass: it writes a
- * mask of the fetched positions and the partial of their exact terms (into
- * a spare workspace slot); the split pass leaves the masked positions out
- * of row t_exact, and the log-sum-exp merge adds the exact partial.  (No
- * quantized term is subtracted, so the row stays accurate when a fetched
- * token held most of its low-bit attention mass.)
+ *   rows_ready: NULL, or a hipEvent_t recorded (on any stream) after
+ *        k_exact/v_exact are written: the call reads idx at once but waits
+ *        for the event only before the launch that reads the rows, so a
+ *        transfer of the rows (kv_fetch_rows on another stream) overlaps
+ *        the split pass ([SC] Approach: the fetch runs in parallel with
+ *        computation).  With NULL the rows must be ready in stream order.
+ * Two more launches than kv_attn_verify: a mask of the fetched positions
+ * before the split pass, which leaves them out of row t_exact, and the
+ * partial of their exact terms after it (into a spare workspace slot),
+ * which the log-sum-exp merge adds.  (No quantized term is subtracted, so
+ * the row stays accurate when a fetched token held most of its low-bit
+ * attention mass.)
  * Requires 0 <= n <= 256. */
 int kv_attn_verify_exact(const kvq_cache* c, const void* q, int T, int Hq,
                          int path, float sm_scale, int t_exact,
                          const int32_t* idx, int n, const void* k_exact,
                          const void* v_exact, void* out, float* lse, void* ws,
-                         size_t ws_bytes, void* stream);
+                         size_t ws_bytes, void* rows_ready, void* stream);
 
 /* Workspace bytes kv_topk needs for this cache at any fill level. */
 size_t kv_topk_workspace_bytes(const kvq_cache* c, int Hq, int k);

@@ -92,7 +92,7 @@ def lib() -> ctypes.CDLL:
     L.kv_topk.argtypes = [P, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     L.kv_dequant_gather.argtypes = [P, vp, i32, i32, vp, vp, vp]
     L.kv_attn_verify_exact.argtypes = [P, vp, i32, i32, i32, f32, i32, vp, i32,
-                                       vp, vp, vp, vp, vp, sz, vp]
+                                       vp, vp, vp, vp, vp, sz, vp, vp]
     L.kv_fetch_rows.argtypes = [P, vp, vp, ctypes.c_int64, vp, i32, vp, vp, vp]
     L.kv_last_error.argtypes = []
     L.kv_last_error.restype = ctypes.c_char_p
@@ -179,11 +179,15 @@ def kv_dequant_gather(c: KvqCacheStruct, idx, n: int, path, k_out, v_out,
 
 def kv_attn_verify_exact(c: KvqCacheStruct, q, T: int, Hq: int, path,
                          sm_scale: float, t_exact: int, idx, n: int, k_exact,
-                         v_exact, out, lse, ws, stream=None) -> None:
+                         v_exact, out, lse, ws, stream=None,
+                         rows_ready=None) -> None:
+    """rows_ready: None, or an event (torch.cuda.Event or a raw hipEvent_t)
+    recorded after k_exact/v_exact were written."""
+    ev = getattr(rows_ready, "cuda_event", rows_ready)
     _check(lib().kv_attn_verify_exact(
         ctypes.byref(c), _ptr(q), T, Hq, _path(path), float(sm_scale), t_exact,
         _ptr(idx), n, _ptr(k_exact), _ptr(v_exact), _ptr(out), _ptr(lse),
-        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+        _ptr(ws), 0 if ws is None else ws.numel(), ev, _stream(stream)))
 
 
 def kv_fetch_rows(c: KvqCacheStruct, host_k, host_v, host_len: int, idx, n: int,
@@ -314,10 +318,12 @@ class QuantKVCache:
 
     def verify_exact(self, q, idx, k_exact, v_exact, t_exact=0, path="target",
                      sm_scale=None, out=None, lse=None, ws=None, want_lse=False,
-                     stream=None):
+                     stream=None, rows_ready=None):
         """kv_attn_verify_exact: like ``verify``, with query row t_exact
         reading k_exact/v_exact [B][Hkv][n][d] at positions idx
-        [B][Hkv][n]; returns (out, lse)."""
+        [B][Hkv][n]; rows_ready: an event recorded after k_exact/v_exact
+        were written (they may still be in flight on another stream), or
+        None; returns (out, lse)."""
         import torch
         s = self.shape
         if (q.dtype != torch.float16 or not q.is_cuda or not q.is_contiguous()
@@ -342,7 +348,7 @@ class QuantKVCache:
         if ws is None:
             ws = self.attn_workspace(T, Hq)
         kv_attn_verify_exact(self.c, q, T, Hq, path, sm_scale, t_exact, idx, n,
-                             k_exact, v_exact, out, lse, ws, stream)
+                             k_exact, v_exact, out, lse, ws, stream, rows_ready)
         return out, lse
 
     def topk_workspace(self, Hq: int, k: int):

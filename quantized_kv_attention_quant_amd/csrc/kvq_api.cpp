@@ -237,6 +237,7 @@ int attn_setup(const kvq_cache* c, const void* q, int T, int Hq, int path,
   a.idx_exact = nullptr;
   a.k_exact = a.v_exact = nullptr;
   a.xmask = nullptr;
+  a.rows_ready = nullptr;
   return KVQ_OK;
 }
 
@@ -284,7 +285,8 @@ KVQ_API int kv_attn_verify_exact(const kvq_cache* c, const void* q, int T, int H
                                  int path, float sm_scale, int t_exact,
                                  const int32_t* idx, int n, const void* k_exact,
                                  const void* v_exact, void* out, float* lse,
-                                 void* ws, size_t ws_bytes, void* stream) {
+                                 void* ws, size_t ws_bytes, void* rows_ready,
+                                 void* stream) {
   kvq::AttnArgs a;
   const int rc = attn_setup(c, q, T, Hq, path, sm_scale, out, lse, ws, ws_bytes, a);
   if (rc) return rc;
@@ -299,6 +301,7 @@ KVQ_API int kv_attn_verify_exact(const kvq_cache* c, const void* q, int T, int H
   a.k_exact = (const __half*)k_exact;
   a.v_exact = (const __half*)v_exact;
   a.xmask = (unsigned*)((char*)ws + partial_bytes(c, T, Hq));
+  a.rows_ready = rows_ready;
   hipError_t e = kvq::launch_attn(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_attn_verify_exact launch");
   return KVQ_OK;

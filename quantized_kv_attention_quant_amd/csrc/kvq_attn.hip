@@ -376,15 +376,18 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
     a.lse[((int64_t)b * a.Hq + h) * a.T + t] = (M + __log2f(lsum)) * kLn2;
 }
 
-// Exact substitution, one workgroup per (group of up to HB GQA heads, kv
-// head, batch) (SpeCache page, Approach: the fetched pairs are used in full
-// precision for the output token).  It runs before the split pass and
-// writes two things:
-//   * the block's mask of fetched positions, one bit per quantized token
-//     (word t covers tile t), which the split pass reads to leave those
-//     positions out of query row t_exact's attention;
-//   * the partial of the fetched tokens' exact terms for row t_exact of each
-//     head, with logits se_j in the log2 domain from the exact keys:
+// Exact substitution (SpeCache page, Approach: the fetched pairs are used
+// in full precision for the output token), in two kernels around the split
+// pass:
+//   * mask_kernel, before it, one workgroup per block: the block's mask of
+//     fetched positions, one bit per quantized token (word t covers tile t),
+//     which the split pass reads to leave those positions out of query row
+//     t_exact's attention.  It needs the positions only, not the fetched
+//     rows, so their transfer can still be in flight.
+//   * exact_kernel, after it, one workgroup per (group of up to HB GQA
+//     heads, kv head, batch): the partial of the fetched tokens' exact terms
+//     for row t_exact of each head, with logits se_j in the log2 domain from
+//     the exact keys:
 //       m = max_j se_j,  l = sum_j 2^(se_j - m),  o = sum_j 2^(se_j - m) v_j,
 //     into the spare partial slot S of the block, so the log-sum-exp merge
 //     of the S + 1 partials gives the row its attention with the fetched
@@ -400,6 +403,20 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
 // share the loaded rows.  Each wave keeps (m, l, o) per head with the usual
 // rescaling, and the 8 wave states meet in LDS by log-sum-exp.  Skipped
 // entries read stand-in row 0 and are never folded in.
+__global__ void __launch_bounds__(256) mask_kernel(const AttnArgs a) {
+  constexpr int NT = 256;
+  const int64_t blk = (int64_t)blockIdx.y * a.g.Hkv + blockIdx.x;
+  unsigned* mw = a.xmask + blk * (a.g.L_max / kTile);
+  const int nw = (int)(a.n_q / kTile);
+  for (int w = threadIdx.x; w < nw; w += NT) mw[w] = 0u;
+  __syncthreads();
+  const int32_t* idx = a.idx_exact + blk * a.n_exact;
+  for (int i = threadIdx.x; i < a.n_exact; i += NT) {
+    const int p = idx[i];
+    if (p >= 0 && p < a.n_q) atomicOr(mw + (p >> 5), 1u << (p & 31));
+  }
+}
+
 template <int D, int RP>
 __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
   constexpr int NT = 512, HB = 4;                // heads per workgroup
@@ -420,17 +437,6 @@ __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
   const __half* ve = a.v_exact + blk * n * D;
 
   for (int i = tid; i < n; i += NT) s_idx[i] = a.idx_exact[blk * n + i];
-  // the block's mask of fetched positions (one workgroup per block writes it)
-  if (blockIdx.x == 0) {
-    unsigned* mw = a.xmask + blk * (g.L_max / kTile);
-    const int nw = (int)(a.n_q / kTile);
-    for (int w = tid; w < nw; w += NT) mw[w] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      const int p = s_idx[i];
-      if (p >= 0 && p < a.n_q) atomicOr(mw + (p >> 5), 1u << (p & 31));
-    }
-  }
   // empty partials for these heads' other query rows
   for (int t = 0; t < a.T; ++t) {
     if (t == a.t_exact) continue;
@@ -1330,11 +1336,11 @@ hipError_t go(AttnArgs a, hipStream_t s) {
   a.grp_shift = -1;
   for (int k = 0; k < 31; ++k)
     if (tpg == 1 << k) a.grp_shift = k;
-  // exact substitution first: it writes the mask of fetched positions the
-  // split pass reads, and the exact-term partial into the spare slot S
+  // exact substitution: the mask of fetched positions first, for the split
+  // pass to read
   if (a.n_exact >= 0) {
-    const dim3 xg((unsigned)cdiv(a.gs, 4), (unsigned)a.g.Hkv, (unsigned)a.g.B);
-    hipLaunchKernelGGL((exact_kernel<D, C::RP>), xg, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(mask_kernel, dim3((unsigned)a.g.Hkv, (unsigned)a.g.B),
+                       dim3(256), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1345,7 +1351,19 @@ hipError_t go(AttnArgs a, hipStream_t s) {
                      dim3(C::NW * kWave), C::LDS, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.n_exact >= 0) ++a.S;     // the merge reads the substitution partial too
+  // then the exact-term partial into the spare slot S, once the fetched
+  // rows are there (rows_ready: an event recorded after their transfer)
+  if (a.n_exact >= 0) {
+    if (a.rows_ready) {
+      e = hipStreamWaitEvent(s, (hipEvent_t)a.rows_ready, 0);
+      if (e != hipSuccess) return e;
+    }
+    const dim3 xg((unsigned)cdiv(a.gs, 4), (unsigned)a.g.Hkv, (unsigned)a.g.B);
+    hipLaunchKernelGGL((exact_kernel<D, C::RP>), xg, dim3(512), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ++a.S;                       // the merge reads the substitution partial too
+  }
   hipLaunchKernelGGL((merge_kernel<D, C::RP>),
                      dim3((unsigned)a.rows, (unsigned)a.g.Hkv, (unsigned)a.g.B),
                      dim3(256), 0, s, a);

@@ -70,43 +70,66 @@ __global__ void __launch_bounds__(kWavesPerGroup * kWave)
   }
 }
 
-// Rows of a full-precision copy of the cache kept in host memory (SpeCache
-// page, Approach: the full KV stays off the GPU and the pairs the
-// speculative token selects are fetched).  One wave per requested row; each
-// lane moves 16 bytes of K and of V straight from host memory (the buffers
-// are device-accessible pinned allocations), so a request of n rows per
-// block crosses the host link once, as 2 * n * d * 2 bytes per block.
-__global__ void __launch_bounds__(kWavesPerGroup * kWave)
+// Rows of the host-resident fp16 copy (SpeCache page, Approach: the KV
+// pairs the speculative token selects are fetched), one request of n rows
+// per block: it crosses the host link once, as 2 * n * d * 2 bytes per block
+// (the buffers are device-accessible pinned allocations).  The transfer is
+// bound by the host link, not the CUs, so a small fixed grid carries it:
+// kFetchGroups workgroups, each wave keeping UR groups of rows in flight
+// (lane piece p of a row moves bytes 16p..16p+15 of its K and V), and the
+// CUs stay free for attention running concurrently on another stream.
+constexpr int kFetchGroups = 8, kFetchWaves = 8;
+
+template <int D>
+__global__ void __launch_bounds__(kFetchWaves * kWave)
     fetch_kernel(const FetchArgs a) {
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const int64_t blk = (int64_t)b * a.Hkv + kvh;
-  const int i = blockIdx.x * kWavesPerGroup + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  if (i >= a.n) return;
-  const int d8 = a.d / 8;                       // 16-byte pieces per row
-  const int64_t p = a.idx[blk * a.n + i];
-  uint4* ko = (uint4*)(a.k_out + (blk * a.n + i) * a.d);
-  uint4* vo = (uint4*)(a.v_out + (blk * a.n + i) * a.d);
-  if (lane >= d8) return;
-  if (p < 0 || p >= a.host_len) {
-    const unsigned nan2 = 0x7e007e00u;
-    ko[lane] = make_uint4(nan2, nan2, nan2, nan2);
-    vo[lane] = make_uint4(nan2, nan2, nan2, nan2);
-    return;
+  constexpr int LPR = D / 8;                    // lanes per row (16 bytes each)
+  constexpr int RPW = kWave / LPR;              // rows per wave per load
+  constexpr int UR = 4;                         // row groups in flight
+  const int64_t total = (int64_t)a.B * a.Hkv * a.n;
+  const int lane = threadIdx.x % kWave, sub = lane / LPR, piece = lane % LPR;
+  const int64_t wave = (int64_t)blockIdx.x * kFetchWaves + threadIdx.x / kWave;
+  const int64_t step = (int64_t)gridDim.x * kFetchWaves * RPW * UR;
+  const unsigned nan2 = 0x7e007e00u;
+  for (int64_t r0 = wave * RPW * UR; r0 < total; r0 += step) {
+    uint4 kx[UR], vx[UR];
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {              // every load first
+      const int64_t r = r0 + u * RPW + sub;     // row blk * n + i
+      kx[u] = vx[u] = make_uint4(nan2, nan2, nan2, nan2);
+      if (r < total) {
+        const int64_t p = a.idx[r];
+        if (p >= 0 && p < a.host_len) {
+          const int64_t blk = r / a.n;
+          const int64_t row = (blk * a.host_len + p) * D;
+          kx[u] = ((const uint4*)(a.host_k + row))[piece];
+          vx[u] = ((const uint4*)(a.host_v + row))[piece];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int64_t r = r0 + u * RPW + sub;
+      if (r < total) {
+        ((uint4*)(a.k_out + r * D))[piece] = kx[u];
+        ((uint4*)(a.v_out + r * D))[piece] = vx[u];
+      }
+    }
   }
-  const int64_t row = (blk * a.host_len + p) * a.d;
-  ko[lane] = ((const uint4*)(a.host_k + row))[lane];
-  vo[lane] = ((const uint4*)(a.host_v + row))[lane];
 }
 
 }  // namespace
 
 hipError_t launch_fetch(const FetchArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(fetch_kernel,
-                     dim3((unsigned)cdiv(a.n, kWavesPerGroup), (unsigned)a.Hkv,
-                          (unsigned)a.B),
-                     dim3(kWavesPerGroup * kWave), 0, s, a);
+  const int64_t rows = (int64_t)a.B * a.Hkv * a.n;
+  const int per_group = kFetchWaves * (kWave / (a.d / 8)) * 4;
+  const unsigned groups = (unsigned)(cdiv(rows, per_group) < kFetchGroups
+                                         ? cdiv(rows, per_group) : kFetchGroups);
+  if (a.d == 128)
+    hipLaunchKernelGGL(fetch_kernel<128>, dim3(groups), dim3(kFetchWaves * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL(fetch_kernel<64>, dim3(groups), dim3(kFetchWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
 

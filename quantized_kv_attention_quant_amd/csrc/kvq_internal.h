@@ -174,6 +174,7 @@ struct AttnArgs {
   const __half* k_exact;    // [B][Hkv][n_exact][d]
   const __half* v_exact;    // [B][Hkv][n_exact][d]
   unsigned* xmask;          // [B*Hkv][L_max/32] fetched-position bits, or NULL
+  void* rows_ready;         // hipEvent_t after k_exact/v_exact are written, or NULL
 };
 // Splits per block for nb blocks on `slots` resident workgroup slots, with
 // `units` units of work per block, nw waves per workgroup, at most cap.
