@@ -191,3 +191,30 @@ def test_value_scale_at_the_limit(bits):
     torch.cuda.synchronize()
     ref, _ = attention.attend(rep, q16, "target", w.d ** -0.5)
     assert_attn_close(out.cpu().numpy(), ref, f"value scale 63, {bits}-bit")
+
+
+@pytest.mark.parametrize("bits", [8, 2])
+def test_quantizer_divide_ties(bits):
+    """The hand-derived groups whose quotient (x - z)/s is an exact
+    half-integer (tests/golden/quant_divide_ties.json), laid along key
+    tokens and value channels: the HIP quantizer must give the correctly
+    rounded divide's codes (a reciprocal-multiply alone would not)."""
+    import json
+    import os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                        "quant_divide_ties.json")))["cases"]
+    case = [c for c in cases if c["bits"] == bits][0]
+    x = np.array(case["x"], np.float16)
+    w = W(f"ties{bits}", 1, 4, 1, 64, 96, 32, 16, 32, bits, "normal")
+    say(f"[gpu] divide ties, {bits}-bit")
+    K, V = host_tokens(w, 1)
+    K[0, :32, 0, :] = np.tile(x, 8)[:, None]             # every key channel
+    V[0, :64, 0, :16] = np.tile(x, 4)[None, :]            # value group 0
+    cache = kq.QuantKVCache(shape_for(w, max_append=96))
+    cache.append(to_dev(K), to_dev(V))
+    rep = ocache.Replay(w.B, w.Hkv, w.d, w.G, w.Gv, w.bits, w.R)
+    rep.append(K, V)
+    torch.cuda.synchronize()
+    assert rep.kq[0, 0, :4, 0].tolist() == case["codes"]
+    assert rep.vq[0, 0, 0, :4].tolist() == case["codes"]
+    assert_block_bytes(cache, 0, 0, rep, 0, 0, f"ties {bits}-bit")
