@@ -119,7 +119,9 @@ __device__ void key_group(const AppendArgs& a, int item, int b, int kvh,
   float mn[CH], mx[CH], x[CH], s[CH], z[CH];
 #pragma unroll
   for (int k = 0; k < CH; ++k) { mn[k] = INFINITY; mx[k] = -INFINITY; }
-  const int slot0 = (int)(ps % g.ring);        // ring slot of ps (one divide)
+  // ring slot of ps (one divide, only when the slice starts in the ring;
+  // appended rows never use it)
+  const int slot0 = ps < a.new0 ? (int)(ps % g.ring) : 0;
   auto slot_of = [&](int tok) {                 // (slot0 + tok) mod ring
     int sl = slot0 + tok;
     while (sl >= g.ring) sl -= g.ring;
@@ -134,16 +136,29 @@ __device__ void key_group(const AppendArgs& a, int item, int b, int kvh,
       mx[k] = fmaxf(mx[k], x[k]);
     }
   }
+  // min/max over the token slices: across the slices of this wave first
+  // (lanes cols, 2 cols, ... apart hold the same channels), then across
+  // the kThreads / 64 waves through LDS
 #pragma unroll
-  for (int k = 0; k < CH; ++k) {
-    s_mn[qt * g.d + c0 + k] = mn[k];
-    s_mx[qt * g.d + c0 + k] = mx[k];
+  for (int k = 0; k < CH; ++k)
+    for (int o = cols; o < kWave; o <<= 1) {
+      mn[k] = fminf(mn[k], __shfl_xor(mn[k], o));
+      mx[k] = fmaxf(mx[k], __shfl_xor(mx[k], o));
+    }
+  const int wv = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) < cols) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      s_mn[wv * g.d + c0 + k] = mn[k];
+      s_mx[wv * g.d + c0 + k] = mx[k];
+    }
   }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < CH; ++k) {
     float lo = INFINITY, hi = -INFINITY;
-    for (int r = 0; r < nq; ++r) {
+#pragma unroll
+    for (int r = 0; r < kThreads / kWave; ++r) {
       lo = fminf(lo, s_mn[r * g.d + c0 + k]);
       hi = fmaxf(hi, s_mx[r * g.d + c0 + k]);
     }
@@ -219,14 +234,14 @@ __device__ void value_tile(const AppendArgs& a, int item, int b, int kvh,
   const int j = threadIdx.x / 8, u = threadIdx.x % 8;
   const int c0 = u * cpv, grp = c0 / g.Gv;
   const int64_t p = p0 + j;
-  const int slot = (int)(p % g.ring);           // one divide per thread
   float x[16];
   if (p >= a.new0) {   // appended token: token-major, 16-byte loads
     const __half* src =
         a.v_new + (((int64_t)b * a.n + (p - a.new0)) * g.Hkv + kvh) * g.d + c0;
     load_chans<8>(src, x);
     if (cpv == 16) load_chans<8>(src + 8, x + 8);
-  } else {
+  } else {             // ring token: one divide per thread for its slot
+    const int slot = (int)(p % g.ring);
 #pragma unroll
     for (int k = 0; k < 16; ++k)
       if (k < cpv) x[k] = value_at(a, b, kvh, p, slot, c0 + k);
