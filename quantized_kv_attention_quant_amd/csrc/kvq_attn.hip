@@ -124,6 +124,24 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
+// fp16 pair (RN16(a * s.lo), RN16(b * t.lo)) of exact fp32 x fp16 products,
+// and the pair of what those leave, RN16(a * s.lo - hi.lo), RN16(b * t.lo -
+// hi.hi): one v_fma_mix each, so hi + lo carries ~22 bits of each product.
+__device__ __forceinline__ unsigned hsplit_hi(float a, unsigned s, float b,
+                                              unsigned t) {
+  h2v r;
+  r[0] = (_Float16)__builtin_fmaf(a, h_lo(s), 0.f);
+  r[1] = (_Float16)__builtin_fmaf(b, h_lo(t), 0.f);
+  return __builtin_bit_cast(unsigned, r);
+}
+__device__ __forceinline__ unsigned hsplit_lo(float a, unsigned s, float b,
+                                              unsigned t, unsigned hi) {
+  h2v r;
+  r[0] = (_Float16)__builtin_fmaf(a, h_lo(s), -h_lo(hi));
+  r[1] = (_Float16)__builtin_fmaf(b, h_lo(t), -h_hi(hi));
+  return __builtin_bit_cast(unsigned, r);
+}
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
 // operations, not for its outstanding global loads (a full __syncthreads
 // would also drain those).
@@ -580,12 +598,18 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   // quotient floor(x W2 / Wt) is taken in fp64, which is exact here (x W2 <
   // 2^40, and a non-integral quotient is at least 1/Wt from an integer) and
   // far cheaper than a 64-bit integer division, which has no instruction.
-  const int W2 = nres + 2 * (U - nres);
+  constexpr int RW = C::RESU / 256;
+  constexpr int QW = C::TPU * ((C::TWO ? 4 : 2) * C::PL + C::VSZB) / 256;
+  const double Wtot = (double)nres * RW + (double)(U - nres) * QW;
   auto bound = [&](int x) __attribute__((always_inline)) {
-    const int w = (int)((double)x * (double)W2 / (double)Wt);
-    int v = w <= nres ? w : nres + (w - nres + 1) / 2;
-    if (v < nres && (v & 1)) ++v;                // keep K/V pairs whole
-    return v;
+    const int64_t w = (int64_t)((double)x * Wtot / (double)Wt);
+    int v;
+    if (w <= (int64_t)nres * RW) {
+      v = (int)((w + RW) / (2 * RW)) * 2;
+    } else {
+      v = nres + (int)((w - (int64_t)nres * RW + QW / 2) / QW);
+    }
+    return v < U ? v : U;
   };
   const int c0s = split * NS;
   // wave-uniform: keep them (and everything derived) in scalar registers
@@ -877,12 +901,11 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
         unsigned hi[4], lo[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // fma with +0 keeps the fp16 operand unconverted (mixed fma)
-          const float xa = opaque(__builtin_fmaf(fa[j], h_lo(sA[j]), 0.f));
-          const float xb = opaque(__builtin_fmaf(fb[j], h_lo(sB[j]), 0.f));
-          hi[j] = pack2(xa, xb);
-          lo[j] = pack2(__builtin_fmaf(h_lo(hi[j]), -1.f, xa),
-                        __builtin_fmaf(h_hi(hi[j]), -1.f, xb));
+          // Q' = q c0 s as fp16 hi + lo, each from the exact product by one
+          // mixed-precision fma (the fp16 s enters unconverted): hi rounds
+          // the product once, lo rounds what hi leaves
+          hi[j] = hsplit_hi(fa[j], sA[j], fb[j], sB[j]);
+          lo[j] = hsplit_lo(fa[j], sA[j], fb[j], sB[j], hi[j]);
           zs[rt] = __builtin_fmaf(fa[j], h_hi(sA[j]), zs[rt]);
           zs[rt] = __builtin_fmaf(fb[j], h_hi(sB[j]), zs[rt]);
         }
