@@ -26,7 +26,10 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-constexpr int kWavesPerGroup = 4;      // attention workgroup = 4 waves
+// Fewest unit streams an attention workgroup runs (8 waves sharing streams in
+// pairs); the split planner gives every stream at least one unit, so no call
+// has more splits than units / kMinStreams.
+constexpr int kMinStreams = 4;
 constexpr int kTopkChunk = 1024;       // tokens per top-k workgroup
 constexpr int kMaxTopk = 256;
 
@@ -92,7 +95,7 @@ int s_alloc_of(const kvq_cache* c) {
   const int64_t ring = round_up((int64_t)c->R + c->max_append, 32);
   const int64_t units_max = 2 * cdiv(ring, 32) + cdiv(c->L_max, 32);
   int64_t s = 4 * cdiv(kSlotsBound, nb);
-  const int64_t by_units = cdiv(units_max, kWavesPerGroup);
+  const int64_t by_units = cdiv(units_max, kMinStreams);
   if (s > by_units) s = by_units;
   if (s > kvq::kMaxSplits - 1) s = kvq::kMaxSplits - 1;
   if (s < 1) s = 1;

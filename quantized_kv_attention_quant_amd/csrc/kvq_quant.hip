@@ -9,15 +9,16 @@
 // One launch covers three kinds of work item (blockIdx.x), each for one
 // (b = blockIdx.z, kvh = blockIdx.y) block:
 //   K-group items: one group of G tokens; thread (t, qt) owns 8 channels
-//     over token slice qt, the slices' min/max meet in LDS, and each thread
-//     writes its slice's codes as whole words of the plane rows.
-//   V-tile items:  32 tokens, 8 threads per token over the channels; a
+//     over token slice qt, the slices' fp16 min/max meet by lane shuffles
+//     and one LDS step, one thread per channel derives (s, z, 1/s), and
+//     each thread writes its slice's codes as whole words of the plane rows.
+//   V-tile items:  32-token tiles, 8 threads per token over the channels; a
 //     value group's min/max meet by lane shuffles; codes are assembled in
 //     LDS into the tiled plane layout and stored with coalesced dword
-//     writes.
+//     writes, the next tile's rows already in flight.
 //   Ring items:    one appended token copied into the fp16 residual ring.
 // The arithmetic is the exact binary32 sequence of the quantizer definition
-// (correctly rounded subtract and divide, round-half-even, RNE to fp16).
+// (correctly rounded subtract and quotient, round-half-even, RNE to fp16).
 #include "kvq_internal.h"
 
 // Bit-exact binary32 arithmetic: built with -ffp-contract=off as well.
@@ -27,6 +28,7 @@ namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+typedef _Float16 hv2 __attribute__((ext_vector_type(2)));   // two fp16 lanes
 
 __device__ inline float stored_scale(float mn, float mx, int Lv) {
   float span = __fsub_rn(mx, mn);
@@ -34,11 +36,30 @@ __device__ inline float stored_scale(float mn, float mx, int Lv) {
   return __half2float(__float2half_rn(s));
 }
 
-__device__ inline unsigned code_of(float x, float z, float s, int Lv) {
+// RN(1/s) of a group's stored scale, once per group (0 for s = 0).
+__device__ inline float recip_of(float s) {
+  return s == 0.f ? 0.f : __fdiv_rn(1.f, s);
+}
+
+// Code of x in a group (z, s), r = RN(1/s): clip(rint(RN((x - z) / s))).
+// The correctly rounded quotient comes without a divide per element:
+// q1 = RN(num r) is within one ulp of num / s, its remainder
+// e = num - q1 s is exact in binary32 (one fma), and RN(q1 + e r) is then
+// the correctly rounded quotient (Markstein's division theorem, which
+// needs r to be the correctly rounded reciprocal and no underflow).  No
+// operand underflows here: num = RN(x - z) of fp16 values is 0 or at
+// least 2^-24, s is an fp16 value, and the quotient is at most 1.5 Lv.
+// An off-line check of every positive fp16 scale against numerators around
+// every k s and (k + 1/2) s, k <= 400, and random ones in [0, 400 s]
+// (2.1e9 cases) found no difference from the divide.
+__device__ inline unsigned code_of(float x, float z, float s, float r, int Lv) {
   if (s == 0.f) return 0u;
-  float r = rintf(__fdiv_rn(__fsub_rn(x, z), s));
-  r = fminf(fmaxf(r, 0.f), (float)Lv);
-  return (unsigned)r;
+  const float num = __fsub_rn(x, z);
+  const float q1 = __fmul_rn(num, r);
+  const float e = __builtin_fmaf(-q1, s, num);
+  float q = rintf(__builtin_fmaf(e, r, q1));
+  q = fminf(fmaxf(q, 0.f), (float)Lv);
+  return (unsigned)q;
 }
 
 // Work items of one launch.  Bulk appends give each V-tile workgroup vt
@@ -62,50 +83,22 @@ __device__ inline const __half* key_row(const AppendArgs& a, int b, int kvh,
   return a.p.k_res + ((int64_t)b * g.Hkv + kvh) * g.res_block + (int64_t)slot * g.d;
 }
 
-// Value channel c of position p, given p's ring slot (p mod ring).
-__device__ inline float value_at(const AppendArgs& a, int b, int kvh,
-                                 int64_t p, int slot, int c) {
-  const CacheGeom& g = a.g;
-  if (p >= a.new0)
-    return __half2float(
-        a.v_new[(((int64_t)b * a.n + (p - a.new0)) * g.Hkv + kvh) * g.d + c]);
-  const __half* base = a.p.v_res + ((int64_t)b * g.Hkv + kvh) * g.res_block +
-                       (int64_t)(slot / kTile) * kTile * g.d;
-  return __half2float(base[vres_index(slot % kTile, c, g.d)]);
-}
-
-// Load CPT consecutive halfs (CPT in {2, 4, 8}) as floats.
-template <int CPT>
-__device__ inline void load_chans(const __half* src, float* out) {
-  constexpr int cpt = CPT;
-  if constexpr (cpt == 2) {
-    __half2 v = *(const __half2*)src;
-    out[0] = __low2float(v); out[1] = __high2float(v);
-  } else if constexpr (cpt == 4) {
-    uint2 raw = *(const uint2*)src;
-    const __half* h = (const __half*)&raw;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) out[k] = __half2float(h[k]);
-  } else {
-    uint4 raw = *(const uint4*)src;
-    const __half* h = (const __half*)&raw;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) out[k] = __half2float(h[k]);
-  }
-}
-
 // K-group item: threads = channel column t (8 consecutive channels, one
-// 16-byte load per token row) x token slice qt (G / NQ consecutive tokens).
-// Each thread takes the min/max of its slice, the slices meet in LDS, and
-// each thread then writes its slice's codes: the 8 channels' codes are one
-// whole word of a plane row (a dword for 8-bit codes in nibble planes, 16
-// bits for 2-bit, a byte for 1-bit).  The token loops are unrolled so
-// several rows are in flight.
+// 16-byte load per token row) x token slice qt (G / nq consecutive tokens).
+// Each thread takes the fp16 min/max of its slice (packed, two channels per
+// instruction: exact), the slices meet by lane shuffles within a wave and
+// through LDS across the waves, one thread per channel then derives the
+// group's (s, z) and RN(1/s) once, and each thread writes its slice's codes:
+// the 8 channels' codes are one whole word of a plane row (a dword for
+// 8-bit codes in nibble planes, 16 bits for 2-bit, a byte for 1-bit).
+// Slices of at most KB tokens stay in registers between the two passes;
+// longer ones are read again in batches of KB rows.
 template <int W>   // bits per code in a plane: 4 (8-bit codes), 2, 1
-__device__ void key_group(const AppendArgs& a, int item, int b, int kvh,
+__device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, int kvh,
                           float* s_mn, float* s_mx) {
   const CacheGeom& g = a.g;
   constexpr int CH = 8;                       // channels per thread
+  constexpr int KB = 8;                       // rows per batch
   constexpr int BITS = W == 4 ? 8 : W;
   const int cols = g.d / CH;                  // channel columns (8 or 16)
   const int nq = kThreads / cols;             // token slices (16 or 32)
@@ -116,9 +109,6 @@ __device__ void key_group(const AppendArgs& a, int item, int b, int kvh,
   const int64_t p0 = a.q0 + (int64_t)item * g.G;
   const int64_t ps = p0 + (int64_t)qt * tpq;
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
-  float mn[CH], mx[CH], x[CH], s[CH], z[CH];
-#pragma unroll
-  for (int k = 0; k < CH; ++k) { mn[k] = INFINITY; mx[k] = -INFINITY; }
   // ring slot of ps (one divide, only when the slice starts in the ring;
   // appended rows never use it)
   const int slot0 = ps < a.new0 ? (int)(ps % g.ring) : 0;
@@ -127,176 +117,258 @@ __device__ void key_group(const AppendArgs& a, int item, int b, int kvh,
     while (sl >= g.ring) sl -= g.ring;
     return sl;
   };
-#pragma unroll 8
-  for (int tok = 0; tok < tpq; ++tok) {
-    load_chans<CH>(key_row(a, b, kvh, ps + tok, slot_of(tok)) + c0, x);
+  auto row = [&](int tok) {
+    return *(const uint4*)(key_row(a, b, kvh, ps + tok, slot_of(tok)) + c0);
+  };
+  hv2 mn[CH / 2], mx[CH / 2];
 #pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      mn[k] = fminf(mn[k], x[k]);
-      mx[k] = fmaxf(mx[k], x[k]);
+  for (int k = 0; k < CH / 2; ++k) {
+    mn[k] = hv2{(_Float16)INFINITY, (_Float16)INFINITY};
+    mx[k] = -mn[k];
+  }
+  auto fold = [&](uint4 r) {
+    const hv2* h = (const hv2*)&r;
+#pragma unroll
+    for (int k = 0; k < CH / 2; ++k) {
+      mn[k] = __builtin_elementwise_min(mn[k], h[k]);
+      mx[k] = __builtin_elementwise_max(mx[k], h[k]);
     }
+  };
+  const bool keep = tpq <= KB;                  // uniform
+  uint4 xr[KB];
+  if (keep) {
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      if (u < tpq) xr[u] = row(u);
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      if (u < tpq) fold(xr[u]);
+  } else {
+#pragma unroll 8
+    for (int tok = 0; tok < tpq; ++tok) fold(row(tok));
   }
   // min/max over the token slices: across the slices of this wave first
   // (lanes cols, 2 cols, ... apart hold the same channels), then across
   // the kThreads / 64 waves through LDS
 #pragma unroll
-  for (int k = 0; k < CH; ++k)
+  for (int k = 0; k < CH / 2; ++k)
     for (int o = cols; o < kWave; o <<= 1) {
-      mn[k] = fminf(mn[k], __shfl_xor(mn[k], o));
-      mx[k] = fmaxf(mx[k], __shfl_xor(mx[k], o));
+      const unsigned lo = __shfl_xor(__builtin_bit_cast(unsigned, mn[k]), o);
+      const unsigned hi = __shfl_xor(__builtin_bit_cast(unsigned, mx[k]), o);
+      mn[k] = __builtin_elementwise_min(mn[k], __builtin_bit_cast(hv2, lo));
+      mx[k] = __builtin_elementwise_max(mx[k], __builtin_bit_cast(hv2, hi));
     }
   const int wv = threadIdx.x / kWave;
+  unsigned* w_mn = (unsigned*)s_mn;             // [wave][d/2] half2 words
+  unsigned* w_mx = (unsigned*)s_mx;
+  float* par = s_mn + 256;                      // [3][d]: s, z, RN(1/s)
   if ((threadIdx.x % kWave) < cols) {
 #pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      s_mn[wv * g.d + c0 + k] = mn[k];
-      s_mx[wv * g.d + c0 + k] = mx[k];
+    for (int k = 0; k < CH / 2; ++k) {
+      w_mn[wv * (g.d / 2) + c0 / 2 + k] = __builtin_bit_cast(unsigned, mn[k]);
+      w_mx[wv * (g.d / 2) + c0 / 2 + k] = __builtin_bit_cast(unsigned, mx[k]);
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int k = 0; k < CH; ++k) {
+  if ((int)threadIdx.x < g.d) {                 // one thread per channel
+    const int c = threadIdx.x;
+    const __half* hmn = (const __half*)w_mn;
+    const __half* hmx = (const __half*)w_mx;
     float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
     for (int r = 0; r < kThreads / kWave; ++r) {
-      lo = fminf(lo, s_mn[r * g.d + c0 + k]);
-      hi = fmaxf(hi, s_mx[r * g.d + c0 + k]);
+      lo = fminf(lo, __half2float(hmn[r * g.d + c]));
+      hi = fmaxf(hi, __half2float(hmx[r * g.d + c]));
     }
-    z[k] = lo;
-    s[k] = stored_scale(lo, hi, Lv);
+    const float sc = stored_scale(lo, hi, Lv);
+    par[c] = sc;
+    par[g.d + c] = lo;
+    par[2 * g.d + c] = recip_of(sc);
+    a.p.k_sz[blk * g.ksz_block + (p0 / g.G) * g.d + c] =
+        __halves2half2(__float2half_rn(sc), __float2half_rn(lo));
   }
-  if (qt == 0) {
-    __half2* ksz = a.p.k_sz + blk * g.ksz_block + (p0 / g.G) * g.d + c0;
+  __syncthreads();
+  float s[CH], z[CH], rs[CH];
 #pragma unroll
-    for (int k = 0; k < CH; ++k)
-      ksz[k] = __halves2half2(__float2half_rn(s[k]), __float2half_rn(z[k]));
+  for (int k = 0; k < CH; ++k) {
+    s[k] = par[c0 + k];
+    z[k] = par[g.d + c0 + k];
+    rs[k] = par[2 * g.d + c0 + k];
   }
   // byte offset of the column's word in a plane row
   uint8_t* hi = a.p.k_hi + blk * g.k_block_bytes + c0 * W / 8;
   uint8_t* lo = BITS == 8 ? a.p.k_lo + blk * g.k_block_bytes + c0 * W / 8 : nullptr;
-  // codes in batches of KB tokens: the batch's rows are loaded before its
-  // codes are stored (the compiler cannot reorder a load above a store that
-  // may alias it, so token-by-token the loads would wait in turn)
-  constexpr int KB = 8;
-  for (int t0 = 0; t0 < tpq; t0 += KB) {
-    float xb[KB][CH];
+  auto emit = [&](int tok, uint4 r) {
+    const int64_t p = ps + tok;
+    const __half* h = (const __half*)&r;
+    unsigned bh = 0, bl = 0;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const unsigned q = code_of(__half2float(h[k]), z[k], s[k], rs[k], Lv);
+      if constexpr (BITS == 8) {
+        bh |= (q >> 4) << (4 * k);
+        bl |= (q & 15u) << (4 * k);
+      } else {
+        bh |= q << (W * k);
+      }
+    }
+    if constexpr (W == 4) {
+      *(unsigned*)(hi + p * g.k_row_bytes) = bh;
+      *(unsigned*)(lo + p * g.k_row_bytes) = bl;
+    } else if constexpr (W == 2) {
+      *(unsigned short*)(hi + p * g.k_row_bytes) = (unsigned short)bh;
+    } else {
+      hi[p * g.k_row_bytes] = (uint8_t)bh;
+    }
+  };
+  if (keep) {
 #pragma unroll
     for (int u = 0; u < KB; ++u)
-      if (t0 + u < tpq)
-        load_chans<CH>(key_row(a, b, kvh, ps + t0 + u, slot_of(t0 + u)) + c0, xb[u]);
+      if (u < tpq) emit(u, xr[u]);
+    return;
+  }
+  // long slices: codes in batches of KB tokens, the batch's rows loaded
+  // before its codes are stored (the compiler cannot reorder a load above a
+  // store that may alias it, so token-by-token the loads would wait in turn)
+  for (int t0 = 0; t0 < tpq; t0 += KB) {
+    uint4 xb[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      if (t0 + u < tpq) xb[u] = row(t0 + u);
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       if (t0 + u >= tpq) break;
-      const int64_t p = ps + t0 + u;
-      unsigned bh = 0, bl = 0;
-#pragma unroll
-      for (int k = 0; k < CH; ++k) {
-        unsigned q = code_of(xb[u][k], z[k], s[k], Lv);
-        if constexpr (BITS == 8) {
-          bh |= (q >> 4) << (4 * k);
-          bl |= (q & 15u) << (4 * k);
-        } else {
-          bh |= q << (W * k);
-        }
-      }
-      if constexpr (W == 4) {
-        *(unsigned*)(hi + p * g.k_row_bytes) = bh;
-        *(unsigned*)(lo + p * g.k_row_bytes) = bl;
-      } else if constexpr (W == 2) {
-        *(unsigned short*)(hi + p * g.k_row_bytes) = (unsigned short)bh;
-      } else {
-        hi[p * g.k_row_bytes] = (uint8_t)bh;
-      }
+      emit(t0 + u, xb[u]);
     }
   }
 }
 
-// V-tile item: 32 tokens, 8 threads per token; thread (j, u) holds the d/8
-// channels u*d/8 .. of token j, a value group spans Gv/(d/8) threads whose
-// min/max meet by lane shuffles.  Codes are assembled in LDS into the tiled
-// plane layout and stored with coalesced dword writes.
-__device__ void value_tile(const AppendArgs& a, int item, int b, int kvh,
-                           unsigned* lds_hi, unsigned* lds_lo) {
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a full __syncthreads
+// would also drain the next tile's prefetched rows).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// V-tile items: `count` consecutive 32-token tiles from tile `first`, 8
+// threads per token; thread (j, u) holds the CPV = D/8 channels u*CPV.. of
+// token j, a value group spans Gv/CPV threads whose min/max meet by lane
+// shuffles.  Codes are assembled in LDS into the tiled plane layout and
+// stored with coalesced dword writes.  The next tile's rows are loaded
+// before the current tile is processed, so their latency overlaps it.
+template <int D, int W>   // head dim; bits per code in a plane
+__device__ __forceinline__ void value_tiles(const AppendArgs& a, int first,
+                                            int count, int b, int kvh,
+                                            unsigned* lds_hi, unsigned* lds_lo) {
   const CacheGeom& g = a.g;
-  const int Lv = (1 << g.bits) - 1;
-  const int ng = g.d / g.Gv;
-  const int words = g.d * g.w;             // dwords per plane tile
-  const int cpv = g.d / 8;                 // channels per thread (8 or 16)
-  const int tpg = g.Gv / cpv;              // threads per value group (1..8)
-  const int64_t p0 = a.q0 + (int64_t)item * kTile;
-  const int64_t tile = p0 / kTile;
+  constexpr int BITS = W == 4 ? 8 : W;
+  constexpr int Lv = (1 << BITS) - 1;
+  constexpr int CPV = D / 8;               // channels per thread (8 or 16)
+  constexpr int NL = CPV / 8;              // 16-byte row pieces per thread
+  constexpr int WORDS = D * W;             // dwords per plane tile
+  constexpr int PER = 4 / W;               // 16-channel groups per dword
+  const int ng = D / g.Gv;
+  const int tpg = g.Gv / CPV;              // threads per value group (1..8)
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
-  for (int i = threadIdx.x; i < words; i += kThreads) {
-    lds_hi[i] = 0u;
-    lds_lo[i] = 0u;
-  }
-  __syncthreads();
   const int j = threadIdx.x / 8, u = threadIdx.x % 8;
-  const int c0 = u * cpv, grp = c0 / g.Gv;
-  const int64_t p = p0 + j;
-  float x[16];
-  if (p >= a.new0) {   // appended token: token-major, 16-byte loads
-    const __half* src =
-        a.v_new + (((int64_t)b * a.n + (p - a.new0)) * g.Hkv + kvh) * g.d + c0;
-    load_chans<8>(src, x);
-    if (cpv == 16) load_chans<8>(src + 8, x + 8);
-  } else {             // ring token: one divide per thread for its slot
-    const int slot = (int)(p % g.ring);
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (k < cpv) x[k] = value_at(a, b, kvh, p, slot, c0 + k);
-  }
-  float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    if (k < cpv) {
-      mn = fminf(mn, x[k]);
-      mx = fmaxf(mx, x[k]);
-    }
-  }
-  for (int o = 1; o < tpg; o <<= 1) {      // lanes of one group: aligned runs
-    mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-  }
-  const float z = mn, s = stored_scale(mn, mx, Lv);
+  const int c0 = u * CPV, grp = c0 / g.Gv;
   const int gg = (j & 15) >> 2, i = j & 3, h = j >> 4;
-  if (u % tpg == 0) {
-    // [part][g][i][group][h]: scale plane then zero-point plane
-    __half* sz = (__half*)(a.p.v_sz + blk * g.vsz_block + tile * g.vsz_tile);
-    const int at = ((gg * 4 + i) * ng + grp) * 2 + h;
-    sz[at] = __float2half_rn(s);
-    sz[32 * ng + at] = __float2half_rn(z);
-  }
-  const int per = 4 / g.w;
+  // fp16 channels c0.. of token j of tile tl (appended rows: 16-byte
+  // loads; ring rows: the permuted ring layout, one divide for the slot)
+  auto load = [&](int tl, uint4 (&xr)[NL]) {
+    const int64_t p = a.q0 + (int64_t)tl * kTile + j;
+    if (p >= a.new0) {
+      const uint4* src = (const uint4*)(
+          a.v_new + (((int64_t)b * a.n + (p - a.new0)) * g.Hkv + kvh) * D + c0);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    if (k < cpv) {
-      const int c = c0 + k;
-      const unsigned q = code_of(x[k], z, s, Lv);
+      for (int n = 0; n < NL; ++n) xr[n] = src[n];
+    } else {
+      const int slot = (int)(p % g.ring);
+      const __half* base = a.p.v_res + blk * g.res_block +
+                           (int64_t)(slot / kTile) * kTile * D;
+      unsigned short e[CPV];
+#pragma unroll
+      for (int k = 0; k < CPV; ++k)
+        e[k] = __half_as_ushort(base[vres_index(slot % kTile, c0 + k, D)]);
+#pragma unroll
+      for (int n = 0; n < NL; ++n)
+        xr[n] = uint4{e[8 * n] | (unsigned)e[8 * n + 1] << 16,
+                      e[8 * n + 2] | (unsigned)e[8 * n + 3] << 16,
+                      e[8 * n + 4] | (unsigned)e[8 * n + 5] << 16,
+                      e[8 * n + 6] | (unsigned)e[8 * n + 7] << 16};
+    }
+  };
+  uint4 cur[NL], nxt[NL];
+  load(first, cur);
+  for (int k = 0; k < count; ++k) {
+    const int tl = first + k;
+    const int64_t tile = a.q0 / kTile + tl;  // q0 is a multiple of G
+    if (k + 1 < count) load(tl + 1, nxt);
+    if (k > 0) lds_barrier();              // the last tile's words read out
+    for (int w = threadIdx.x; w < WORDS; w += kThreads) {
+      lds_hi[w] = 0u;
+      if constexpr (BITS == 8) lds_lo[w] = 0u;
+    }
+    // group min/max: packed fp16 (exact), then across the group's lanes
+    hv2 m2 = __builtin_bit_cast(hv2, cur[0].x), x2 = m2;
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      const hv2* hp = (const hv2*)&cur[n];
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        m2 = __builtin_elementwise_min(m2, hp[k2]);
+        x2 = __builtin_elementwise_max(x2, hp[k2]);
+      }
+    }
+    float mn = fminf((float)m2[0], (float)m2[1]);
+    float mx = fmaxf((float)x2[0], (float)x2[1]);
+    for (int o = 1; o < tpg; o <<= 1) {    // lanes of one group: aligned runs
+      mn = fminf(mn, __shfl_xor(mn, o));
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    const float z = mn, sc = stored_scale(mn, mx, Lv), rs = recip_of(sc);
+    if (u % tpg == 0) {
+      // [part][g][i][group][h]: scale plane then zero-point plane
+      __half* sz = (__half*)(a.p.v_sz + blk * g.vsz_block + tile * g.vsz_tile);
+      const int at = ((gg * 4 + i) * ng + grp) * 2 + h;
+      sz[at] = __float2half_rn(sc);
+      sz[32 * ng + at] = __float2half_rn(z);
+    }
+    lds_barrier();                           // LDS words cleared
+    const __half* hx = (const __half*)cur;
+#pragma unroll
+    for (int k2 = 0; k2 < CPV; ++k2) {
+      const int c = c0 + k2;
+      const unsigned q = code_of(__half2float(hx[k2]), z, sc, rs, Lv);
       const int r = c & 15, m = c >> 4;
-      const int dw = (16 * gg + r) * (g.d * g.w / 64) + m / per;
-      const int bit = 16 * h + g.w * (4 * (m % per) + i);
-      if (g.bits == 8) {
+      const int dw = (16 * gg + r) * (D * W / 64) + m / PER;
+      const int bit = 16 * h + W * (4 * (m % PER) + i);
+      if constexpr (BITS == 8) {
         atomicOr(&lds_hi[dw], (q >> 4) << bit);
         atomicOr(&lds_lo[dw], (q & 15u) << bit);
       } else {
         atomicOr(&lds_hi[dw], q << bit);
       }
     }
-  }
-  __syncthreads();
-  unsigned* ghi = (unsigned*)(a.p.v_hi + blk * g.v_block_bytes +
-                              tile * g.v_tile_bytes);
-  unsigned* glo = g.bits == 8 ? (unsigned*)(a.p.v_lo + blk * g.v_block_bytes +
-                                            tile * g.v_tile_bytes)
-                              : nullptr;
-  for (int i = threadIdx.x; i < words; i += kThreads) {
-    ghi[i] = lds_hi[i];
-    if (glo) glo[i] = lds_lo[i];
+    lds_barrier();                           // the tile's words complete
+    unsigned* ghi = (unsigned*)(a.p.v_hi + blk * g.v_block_bytes +
+                                tile * g.v_tile_bytes);
+    unsigned* glo = (unsigned*)(a.p.v_lo + blk * g.v_block_bytes +
+                                tile * g.v_tile_bytes);
+    for (int w = threadIdx.x; w < WORDS; w += kThreads) {
+      ghi[w] = lds_hi[w];
+      if constexpr (BITS == 8) glo[w] = lds_lo[w];
+    }
+    if (k + 1 < count) {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) cur[n] = nxt[n];
+    }
   }
 }
 
-__device__ void ring_token(const AppendArgs& a, int item, int b, int kvh) {
+__device__ __forceinline__ void ring_token(const AppendArgs& a, int item, int b, int kvh) {
   const CacheGeom& g = a.g;
   const int ni = a.wr_first + item;
   const int64_t p = a.new0 + ni;
@@ -317,7 +389,8 @@ __global__ void __launch_bounds__(kThreads)
 append_kernel(AppendArgs a, Item it) {
   __shared__ unsigned lds_hi[128 * 4];
   __shared__ unsigned lds_lo[128 * 4];
-  __shared__ float s_mn[16 * 128], s_mx[16 * 128];   // K slices' min/max
+  // K groups: the waves' fp16 min/max words, then the channels' (s, z, 1/s)
+  __shared__ float s_mn[256 + 3 * 128], s_mx[256];
   const int b = blockIdx.z, kvh = blockIdx.y;
   int x = blockIdx.x;
   if (x < it.k_items) {
@@ -328,11 +401,15 @@ append_kernel(AppendArgs a, Item it) {
   }
   x -= it.k_items;
   if (x < it.v_items) {
-    for (int k = 0; k < it.vt; ++k) {
-      const int tl = x * it.vt + k;
-      if (tl >= it.v_tiles) break;              // uniform in the workgroup
-      if (k > 0) __syncthreads();               // LDS of the last tile read out
-      value_tile(a, tl, b, kvh, lds_hi, lds_lo);
+    const int first = x * it.vt;
+    const int count = min(it.vt, it.v_tiles - first);
+    if (a.g.d == 128) {
+      if (a.g.w == 4) value_tiles<128, 4>(a, first, count, b, kvh, lds_hi, lds_lo);
+      else if (a.g.w == 2) value_tiles<128, 2>(a, first, count, b, kvh, lds_hi, lds_lo);
+      else value_tiles<128, 1>(a, first, count, b, kvh, lds_hi, lds_lo);
+    } else {   // d = 64: 8-bit or 2-bit codes
+      if (a.g.w == 4) value_tiles<64, 4>(a, first, count, b, kvh, lds_hi, lds_lo);
+      else value_tiles<64, 2>(a, first, count, b, kvh, lds_hi, lds_lo);
     }
     return;
   }
