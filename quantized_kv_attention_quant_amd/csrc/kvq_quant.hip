@@ -36,14 +36,16 @@ __device__ inline float stored_scale(float mn, float mx, int Lv) {
   return __half2float(__float2half_rn(s));
 }
 
-// RN(1/s) of a group's stored scale, once per group (0 for s = 0).
+// RN(1/s) of a group's stored scale, once per group; 0 for s = 0, which
+// makes every code of the group 0 in code_word below.
 __device__ inline float recip_of(float s) {
   return s == 0.f ? 0.f : __fdiv_rn(1.f, s);
 }
 
-// Code of x in a group (z, s), r = RN(1/s): clip(rint(RN((x - z) / s))).
-// The correctly rounded quotient comes without a divide per element:
-// q1 = RN(num r) is within one ulp of num / s, its remainder
+// Code of x in a group (z, s), r = RN(1/s): clip(rint(RN((x - z) / s)))
+// in the low bits of the returned word (the bits above are those of 2^23:
+// mask them off).  The correctly rounded quotient comes without a divide
+// per element: q1 = RN(num r) is within one ulp of num / s, its remainder
 // e = num - q1 s is exact in binary32 (one fma), and RN(q1 + e r) is then
 // the correctly rounded quotient (Markstein's division theorem, which
 // needs r to be the correctly rounded reciprocal and no underflow).  No
@@ -51,15 +53,18 @@ __device__ inline float recip_of(float s) {
 // least 2^-24, s is an fp16 value, and the quotient is at most 1.5 Lv.
 // An off-line check of every positive fp16 scale against numerators around
 // every k s and (k + 1/2) s, k <= 400, and random ones in [0, 400 s]
-// (2.1e9 cases) found no difference from the divide.
-__device__ inline unsigned code_of(float x, float z, float s, float r, int Lv) {
-  if (s == 0.f) return 0u;
-  const float num = __fsub_rn(x, z);
+// (2.1e9 cases) found no difference from the divide.  A degenerate group
+// (s = 0, r = 0) gives q1 = 0, e = num and a quotient of 0: no branch.
+// The clip comes before the rounding (0 and Lv are integers, so the two
+// commute), and the rounding is the add of 2^23, which rounds a value in
+// [0, 2^22] to an integer, ties to even, exactly as rint does.
+__device__ inline unsigned code_word(float x, float z, float s, float r,
+                                     float Lv) {
+  const float num = __builtin_fmaf(x, 1.f, -z);      // RN(x - z)
   const float q1 = __fmul_rn(num, r);
   const float e = __builtin_fmaf(-q1, s, num);
-  float q = rintf(__builtin_fmaf(e, r, q1));
-  q = fminf(fmaxf(q, 0.f), (float)Lv);
-  return (unsigned)q;
+  const float q = __builtin_fmaf(e, r, q1);
+  return __float_as_uint(__fadd_rn(fminf(fmaxf(q, 0.f), Lv), 8388608.f));
 }
 
 // Work items of one launch.  Bulk appends give each V-tile workgroup vt
@@ -93,15 +98,16 @@ __device__ inline const __half* key_row(const AppendArgs& a, int b, int kvh,
 // 8-bit codes in nibble planes, 16 bits for 2-bit, a byte for 1-bit).
 // Slices of at most KB tokens stay in registers between the two passes;
 // longer ones are read again in batches of KB rows.
-template <int W>   // bits per code in a plane: 4 (8-bit codes), 2, 1
+template <int D, int W>   // head dim; bits per code in a plane: 4 (8-bit codes), 2, 1
 __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, int kvh,
                           float* s_mn, float* s_mx) {
   const CacheGeom& g = a.g;
   constexpr int CH = 8;                       // channels per thread
   constexpr int KB = 8;                       // rows per batch
   constexpr int BITS = W == 4 ? 8 : W;
-  const int cols = g.d / CH;                  // channel columns (8 or 16)
-  const int nq = kThreads / cols;             // token slices (16 or 32)
+  constexpr int cols = D / CH;                // channel columns (8 or 16)
+  constexpr int nq = kThreads / cols;         // token slices (16 or 32)
+  constexpr int RB = D * W / 8;               // bytes per plane row
   const int tpq = g.G / nq;                   // tokens per slice (>= 1)
   const int t = threadIdx.x % cols, qt = threadIdx.x / cols;
   const int c0 = t * CH;
@@ -165,26 +171,26 @@ __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, 
   if ((threadIdx.x % kWave) < cols) {
 #pragma unroll
     for (int k = 0; k < CH / 2; ++k) {
-      w_mn[wv * (g.d / 2) + c0 / 2 + k] = __builtin_bit_cast(unsigned, mn[k]);
-      w_mx[wv * (g.d / 2) + c0 / 2 + k] = __builtin_bit_cast(unsigned, mx[k]);
+      w_mn[wv * (D / 2) + c0 / 2 + k] = __builtin_bit_cast(unsigned, mn[k]);
+      w_mx[wv * (D / 2) + c0 / 2 + k] = __builtin_bit_cast(unsigned, mx[k]);
     }
   }
   __syncthreads();
-  if ((int)threadIdx.x < g.d) {                 // one thread per channel
+  if ((int)threadIdx.x < D) {                 // one thread per channel
     const int c = threadIdx.x;
     const __half* hmn = (const __half*)w_mn;
     const __half* hmx = (const __half*)w_mx;
     float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
     for (int r = 0; r < kThreads / kWave; ++r) {
-      lo = fminf(lo, __half2float(hmn[r * g.d + c]));
-      hi = fmaxf(hi, __half2float(hmx[r * g.d + c]));
+      lo = fminf(lo, __half2float(hmn[r * D + c]));
+      hi = fmaxf(hi, __half2float(hmx[r * D + c]));
     }
     const float sc = stored_scale(lo, hi, Lv);
     par[c] = sc;
-    par[g.d + c] = lo;
-    par[2 * g.d + c] = recip_of(sc);
-    a.p.k_sz[blk * g.ksz_block + (p0 / g.G) * g.d + c] =
+    par[D + c] = lo;
+    par[2 * D + c] = recip_of(sc);
+    a.p.k_sz[blk * g.ksz_block + (p0 / g.G) * D + c] =
         __halves2half2(__float2half_rn(sc), __float2half_rn(lo));
   }
   __syncthreads();
@@ -192,8 +198,8 @@ __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, 
 #pragma unroll
   for (int k = 0; k < CH; ++k) {
     s[k] = par[c0 + k];
-    z[k] = par[g.d + c0 + k];
-    rs[k] = par[2 * g.d + c0 + k];
+    z[k] = par[D + c0 + k];
+    rs[k] = par[2 * D + c0 + k];
   }
   // byte offset of the column's word in a plane row
   uint8_t* hi = a.p.k_hi + blk * g.k_block_bytes + c0 * W / 8;
@@ -204,21 +210,21 @@ __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, 
     unsigned bh = 0, bl = 0;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const unsigned q = code_of(__half2float(h[k]), z[k], s[k], rs[k], Lv);
+      const unsigned q = code_word(__half2float(h[k]), z[k], s[k], rs[k], (float)Lv);
       if constexpr (BITS == 8) {
-        bh |= (q >> 4) << (4 * k);
+        bh |= ((q >> 4) & 15u) << (4 * k);
         bl |= (q & 15u) << (4 * k);
       } else {
-        bh |= q << (W * k);
+        bh |= (q & (unsigned)Lv) << (W * k);
       }
     }
     if constexpr (W == 4) {
-      *(unsigned*)(hi + p * g.k_row_bytes) = bh;
-      *(unsigned*)(lo + p * g.k_row_bytes) = bl;
+      *(unsigned*)(hi + p * RB) = bh;
+      *(unsigned*)(lo + p * RB) = bl;
     } else if constexpr (W == 2) {
-      *(unsigned short*)(hi + p * g.k_row_bytes) = (unsigned short)bh;
+      *(unsigned short*)(hi + p * RB) = (unsigned short)bh;
     } else {
-      hi[p * g.k_row_bytes] = (uint8_t)bh;
+      hi[p * RB] = (uint8_t)bh;
     }
   };
   if (keep) {
@@ -341,7 +347,7 @@ __device__ __forceinline__ void value_tiles(const AppendArgs& a, int first,
 #pragma unroll
     for (int k2 = 0; k2 < CPV; ++k2) {
       const int c = c0 + k2;
-      const unsigned q = code_of(__half2float(hx[k2]), z, sc, rs, Lv);
+      const unsigned q = code_word(__half2float(hx[k2]), z, sc, rs, (float)Lv) & 255u;
       const int r = c & 15, m = c >> 4;
       const int dw = (16 * gg + r) * (D * W / 64) + m / PER;
       const int bit = 16 * h + W * (4 * (m % PER) + i);
@@ -394,9 +400,14 @@ append_kernel(AppendArgs a, Item it) {
   const int b = blockIdx.z, kvh = blockIdx.y;
   int x = blockIdx.x;
   if (x < it.k_items) {
-    if (a.g.w == 4) key_group<4>(a, x, b, kvh, s_mn, s_mx);
-    else if (a.g.w == 2) key_group<2>(a, x, b, kvh, s_mn, s_mx);
-    else key_group<1>(a, x, b, kvh, s_mn, s_mx);
+    if (a.g.d == 128) {
+      if (a.g.w == 4) key_group<128, 4>(a, x, b, kvh, s_mn, s_mx);
+      else if (a.g.w == 2) key_group<128, 2>(a, x, b, kvh, s_mn, s_mx);
+      else key_group<128, 1>(a, x, b, kvh, s_mn, s_mx);
+    } else {   // d = 64: 8-bit or 2-bit codes
+      if (a.g.w == 4) key_group<64, 4>(a, x, b, kvh, s_mn, s_mx);
+      else key_group<64, 2>(a, x, b, kvh, s_mn, s_mx);
+    }
     return;
   }
   x -= it.k_items;
