@@ -36,6 +36,12 @@ __device__ inline float stored_scale(float mn, float mx, int Lv) {
   return __half2float(__float2half_rn(s));
 }
 
+// Key groups per K item: when G divides 128 (head dim 128), 128/G groups
+// side by side, so every group's threads hold 8 rows each; else one.
+__host__ __device__ inline int kgroups_per_item(int d, int G) {
+  return (d == 128 && G < 128 && 128 % G == 0) ? 128 / G : 1;
+}
+
 // RN(1/s) of a group's stored scale, once per group; 0 for s = 0, which
 // makes every code of the group 0 in code_word below.
 __device__ inline float recip_of(float s) {
@@ -88,17 +94,19 @@ __device__ inline const __half* key_row(const AppendArgs& a, int b, int kvh,
   return a.p.k_res + ((int64_t)b * g.Hkv + kvh) * g.res_block + (int64_t)slot * g.d;
 }
 
-// K-group item: threads = channel column t (8 consecutive channels, one
-// 16-byte load per token row) x token slice qt (G / nq consecutive tokens).
-// Each thread takes the fp16 min/max of its slice (packed, two channels per
+// K-group item: kgroups_per_item(d, G) key groups of G tokens side by side,
+// each in its own run of threads, thread = channel column t (8 consecutive
+// channels, one 16-byte load per token row) x token slice qt.  Each thread
+// takes the fp16 min/max of its slice (packed, two channels per
 // instruction: exact), the slices meet by lane shuffles within a wave and
-// through LDS across the waves, one thread per channel then derives the
-// group's (s, z) and RN(1/s) once, and each thread writes its slice's codes:
-// the 8 channels' codes are one whole word of a plane row (a dword for
-// 8-bit codes in nibble planes, 16 bits for 2-bit, a byte for 1-bit).
+// through LDS across the group's waves, one thread per channel then derives
+// the group's (s, z) and RN(1/s) once, and each thread writes its slice's
+// codes: the 8 channels' codes are one whole word of a plane row (a dword
+// for 8-bit codes in nibble planes, 16 bits for 2-bit, a byte for 1-bit).
 // Slices of at most KB tokens stay in registers between the two passes;
 // longer ones are read again in batches of KB rows.
-template <int D, int W>   // head dim; bits per code in a plane: 4 (8-bit codes), 2, 1
+template <int D, int W, int NGI>   // head dim; bits per code in a plane:
+                                   // 4 (8-bit codes), 2, 1; groups per item
 __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, int kvh,
                           float* s_mn, float* s_mx) {
   const CacheGeom& g = a.g;
@@ -106,18 +114,22 @@ __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, 
   constexpr int KB = 8;                       // rows per batch
   constexpr int BITS = W == 4 ? 8 : W;
   constexpr int cols = D / CH;                // channel columns (8 or 16)
-  constexpr int nq = kThreads / cols;         // token slices (16 or 32)
   constexpr int RB = D * W / 8;               // bytes per plane row
-  const int tpq = g.G / nq;                   // tokens per slice (>= 1)
-  const int t = threadIdx.x % cols, qt = threadIdx.x / cols;
+  constexpr int tps = kThreads / NGI;         // threads per group (>= 64)
+  const int sg = threadIdx.x / tps, ti = threadIdx.x % tps;
+  constexpr int wps = tps / kWave;            // waves per group
+  const int tpq = g.G / (tps / cols);         // tokens per slice (>= 1)
+  const int t = ti % cols, qt = ti / cols;
   const int c0 = t * CH;
   constexpr int Lv = (1 << BITS) - 1;
-  const int64_t p0 = a.q0 + (int64_t)item * g.G;
+  const int gi = item * NGI + sg;             // this run's key group
+  const bool valid = gi < a.groups;           // the last item may be short
+  const int64_t p0 = a.q0 + (int64_t)gi * g.G;
   const int64_t ps = p0 + (int64_t)qt * tpq;
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
   // ring slot of ps (one divide, only when the slice starts in the ring;
   // appended rows never use it)
-  const int slot0 = ps < a.new0 ? (int)(ps % g.ring) : 0;
+  const int slot0 = valid && ps < a.new0 ? (int)(ps % g.ring) : 0;
   auto slot_of = [&](int tok) {                 // (slot0 + tok) mod ring
     int sl = slot0 + tok;
     while (sl >= g.ring) sl -= g.ring;
@@ -145,17 +157,17 @@ __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, 
   if (keep) {
 #pragma unroll
     for (int u = 0; u < KB; ++u)
-      if (u < tpq) xr[u] = row(u);
+      if (valid && u < tpq) xr[u] = row(u);
 #pragma unroll
     for (int u = 0; u < KB; ++u)
-      if (u < tpq) fold(xr[u]);
-  } else {
+      if (valid && u < tpq) fold(xr[u]);
+  } else if (valid) {
 #pragma unroll 8
     for (int tok = 0; tok < tpq; ++tok) fold(row(tok));
   }
   // min/max over the token slices: across the slices of this wave first
-  // (lanes cols, 2 cols, ... apart hold the same channels), then across
-  // the kThreads / 64 waves through LDS
+  // (lanes cols, 2 cols, ... apart hold the same channels; a wave lies in
+  // one group), then across the group's waves through LDS
 #pragma unroll
   for (int k = 0; k < CH / 2; ++k)
     for (int o = cols; o < kWave; o <<= 1) {
@@ -167,7 +179,7 @@ __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, 
   const int wv = threadIdx.x / kWave;
   unsigned* w_mn = (unsigned*)s_mn;             // [wave][d/2] half2 words
   unsigned* w_mx = (unsigned*)s_mx;
-  float* par = s_mn + 256;                      // [3][d]: s, z, RN(1/s)
+  float* par = s_mn + 256 + sg * 3 * D;         // [3][d]: s, z, RN(1/s)
   if ((threadIdx.x % kWave) < cols) {
 #pragma unroll
     for (int k = 0; k < CH / 2; ++k) {
@@ -176,13 +188,11 @@ __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, 
     }
   }
   __syncthreads();
-  if ((int)threadIdx.x < D) {                 // one thread per channel
-    const int c = threadIdx.x;
+  for (int c = ti; c < D; c += tps) {           // one thread per channel
     const __half* hmn = (const __half*)w_mn;
     const __half* hmx = (const __half*)w_mx;
     float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < kThreads / kWave; ++r) {
+    for (int r = sg * wps; r < (sg + 1) * wps; ++r) {
       lo = fminf(lo, __half2float(hmn[r * D + c]));
       hi = fmaxf(hi, __half2float(hmx[r * D + c]));
     }
@@ -190,8 +200,9 @@ __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, 
     par[c] = sc;
     par[D + c] = lo;
     par[2 * D + c] = recip_of(sc);
-    a.p.k_sz[blk * g.ksz_block + (p0 / g.G) * D + c] =
-        __halves2half2(__float2half_rn(sc), __float2half_rn(lo));
+    if (valid)
+      a.p.k_sz[blk * g.ksz_block + (p0 / g.G) * D + c] =
+          __halves2half2(__float2half_rn(sc), __float2half_rn(lo));
   }
   __syncthreads();
   float s[CH], z[CH], rs[CH];
@@ -227,6 +238,7 @@ __device__ __forceinline__ void key_group(const AppendArgs& a, int item, int b, 
       hi[p * RB] = (uint8_t)bh;
     }
   };
+  if (!valid) return;
   if (keep) {
 #pragma unroll
     for (int u = 0; u < KB; ++u)
@@ -396,17 +408,28 @@ append_kernel(AppendArgs a, Item it) {
   __shared__ unsigned lds_hi[128 * 4];
   __shared__ unsigned lds_lo[128 * 4];
   // K groups: the waves' fp16 min/max words, then the channels' (s, z, 1/s)
-  __shared__ float s_mn[256 + 3 * 128], s_mx[256];
+  __shared__ float s_mn[256 + 4 * 3 * 128], s_mx[256];
   const int b = blockIdx.z, kvh = blockIdx.y;
   int x = blockIdx.x;
   if (x < it.k_items) {
     if (a.g.d == 128) {
-      if (a.g.w == 4) key_group<128, 4>(a, x, b, kvh, s_mn, s_mx);
-      else if (a.g.w == 2) key_group<128, 2>(a, x, b, kvh, s_mn, s_mx);
-      else key_group<128, 1>(a, x, b, kvh, s_mn, s_mx);
-    } else {   // d = 64: 8-bit or 2-bit codes
-      if (a.g.w == 4) key_group<64, 4>(a, x, b, kvh, s_mn, s_mx);
-      else key_group<64, 2>(a, x, b, kvh, s_mn, s_mx);
+      const int ngi = kgroups_per_item(128, a.g.G);
+      if (ngi == 4) {
+        if (a.g.w == 4) key_group<128, 4, 4>(a, x, b, kvh, s_mn, s_mx);
+        else if (a.g.w == 2) key_group<128, 2, 4>(a, x, b, kvh, s_mn, s_mx);
+        else key_group<128, 1, 4>(a, x, b, kvh, s_mn, s_mx);
+      } else if (ngi == 2) {
+        if (a.g.w == 4) key_group<128, 4, 2>(a, x, b, kvh, s_mn, s_mx);
+        else if (a.g.w == 2) key_group<128, 2, 2>(a, x, b, kvh, s_mn, s_mx);
+        else key_group<128, 1, 2>(a, x, b, kvh, s_mn, s_mx);
+      } else {
+        if (a.g.w == 4) key_group<128, 4, 1>(a, x, b, kvh, s_mn, s_mx);
+        else if (a.g.w == 2) key_group<128, 2, 1>(a, x, b, kvh, s_mn, s_mx);
+        else key_group<128, 1, 1>(a, x, b, kvh, s_mn, s_mx);
+      }
+    } else {   // d = 64: 8-bit or 2-bit codes, one group per item
+      if (a.g.w == 4) key_group<64, 4, 1>(a, x, b, kvh, s_mn, s_mx);
+      else key_group<64, 2, 1>(a, x, b, kvh, s_mn, s_mx);
     }
     return;
   }
@@ -439,7 +462,7 @@ append_kernel(AppendArgs a, Item it) {
 hipError_t launch_append(const AppendArgs& a, bool flush, bool ring_write,
                          hipStream_t s) {
   Item it;
-  it.k_items = flush ? a.groups : 0;
+  it.k_items = flush ? (int)cdiv(a.groups, kgroups_per_item(a.g.d, a.g.G)) : 0;
   it.v_tiles = flush ? (int)((int64_t)a.groups * a.g.G / kTile) : 0;
   it.r_tokens = ring_write ? a.wr_count : 0;
   it.vt = it.v_tiles >= 64 ? 4 : 1;
