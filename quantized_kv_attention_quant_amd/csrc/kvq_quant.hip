@@ -57,9 +57,9 @@ __device__ inline float recip_of(float s) {
 // needs r to be the correctly rounded reciprocal and no underflow).  No
 // operand underflows here: num = RN(x - z) of fp16 values is 0 or at
 // least 2^-24, s is an fp16 value, and the quotient is at most 1.5 Lv.
-// An off-line check of every positive fp16 scale against numerators around
-// every k s and (k + 1/2) s, k <= 400, and random ones in [0, 400 s]
-// (2.1e9 cases) found no difference from the divide.  A degenerate group
+// tests/quotient_identity.c checks this against the divide for every
+// positive fp16 scale, at the numerators around every k s and (k + 1/2) s,
+// k <= 400, and at random ones in [0, 400 s] (2.1e9 cases).  A degenerate group
 // (s = 0, r = 0) gives q1 = 0, e = num and a quotient of 0: no branch.
 // The clip comes before the rounding (0 and Lv are integers, so the two
 // commute), and the rounding is the add of 2^23, which rounds a value in
