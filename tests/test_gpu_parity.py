@@ -41,6 +41,11 @@ SMALL = {
     "g64_bulk": W("g64_bulk", 1, 4, 2, 128, 4560, 64, 64, 64, 8, "outlier"),
     # 10 top-k chunks: top-256 candidates overflow one merge pass
     "long_2bit": W("long_2bit", 1, 8, 2, 128, 9500, 32, 32, 32, 2, "normal"),
+    # key groups longer than 128 tokens: 16 rows per quantizer thread at
+    # head dim 128 (read again in batches of 8), 8 rows at head dim 64
+    "g256": W("g256", 1, 4, 2, 128, 1800, 256, 64, 256, 8, "outlier"),
+    "d64_g256_2bit": W("d64_g256_2bit", 1, 4, 2, 64, 1500, 256, 32, 256, 2,
+                       "normal"),
 }
 
 
@@ -84,7 +89,7 @@ def test_append_bulk_bit_exact(name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "gqa_d128_int8", "gqa_2bit",
-                                  "gqa_1bit", "mha_d64_int8", "g96"])
+                                  "gqa_1bit", "mha_d64_int8", "g96", "g256"])
 def test_append_incremental_and_rollback(name):
     w = SMALL[name]
     say(f"[gpu] append incremental {name}")
@@ -121,7 +126,9 @@ RUNS = [("tiny", "target", 1), ("tiny", "draft4", 1), ("tiny", "target", 8),
         ("g96", "target", 7), ("g96", "draft4", 1), ("g96_2bit", "target", 2),
         # T = 16, the largest speculative block: 16 rows (MHA) and 32 (GQA 2)
         ("mha_d64_int8", "target", 16), ("gqa2", "target", 16),
-        ("gqa2", "draft4", 16)]
+        ("gqa2", "draft4", 16),
+        ("g256", "target", 5), ("g256", "draft4", 1),
+        ("d64_g256_2bit", "target", 3)]
 
 
 @pytest.mark.parametrize("name,path,T", RUNS)
@@ -194,7 +201,8 @@ def test_verify_row_equals_prefix_decode():
     ("gqa_2bit", "target", 64), ("gqa_1bit", "target", 100),
     ("mha_d64_int8", "target", 256), ("tiny", "target", 300 // 2),
     ("g96", "target", 64), ("g96", "draft4", 64), ("g96_2bit", "target", 200),
-    ("g32_bulk", "target", 128), ("long_2bit", "target", 256)])
+    ("g32_bulk", "target", 128), ("long_2bit", "target", 256),
+    ("g256", "target", 64), ("d64_g256_2bit", "target", 32)])
 def test_topk_bit_exact(name, path, k):
     w = SMALL[name]
     say(f"[gpu] topk {name} {path} k={k}")
