@@ -63,11 +63,14 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x,
 // run of every stage k ends ordered and the last one sorts all elements.
 // Runs of k_first / 2 elements that already stand in that order (even runs
 // descending, odd runs ascending) may skip the stages below k_first.
+// With k_last below NTS * 4, the network stops after the stages of k_last:
+// runs of k_last elements, alternately descending and ascending.
 template <int NTS>
 __device__ void sort_regs_desc(unsigned long long (&e)[TPT],
-                               unsigned long long* lds, int k_first = 2) {
+                               unsigned long long* lds, int k_first = 2,
+                               int k_last = NTS * TPT) {
   const int tid = threadIdx.x;
-  for (int k = k_first; k <= NTS * TPT; k <<= 1) {
+  for (int k = k_first; k <= k_last; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       if (j < TPT) {                      // both elements in this thread
 #pragma unroll
@@ -112,6 +115,75 @@ __device__ void sort_regs_desc(unsigned long long (&e)[TPT],
   }
 }
 
+// Workgroup barrier for LDS hand-offs only (no global loads are pending
+// where it is used).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The best P of the workgroup's NT * 4 composites (P a power of two, 4 <= P
+// <= NT * 2), sorted descending into element 4 * tid + m of the first P / 4
+// threads.  The network sorts runs of P (alternately descending and
+// ascending), then halves the live elements level by level: the max of
+// element i of a descending run and element i of the ascending run after
+// it holds the best P of the two (a bitonic sequence), which log2(P)
+// compare-exchange stages sort again.  The survivors of each level move
+// through LDS to the first threads, so the waves left without live
+// elements drop out of the later levels.
+__device__ void chunk_top(unsigned long long (&e)[TPT], unsigned long long* lds,
+                          int P) {
+  const int tid = threadIdx.x;
+  sort_regs_desc<NT>(e, lds, 2, P);
+  for (int live = NT * TPT; live > P; live >>= 1) {
+    lds_barrier();                              // earlier readers of lds done
+    if (TPT * tid < live) {
+#pragma unroll
+      for (int m = 0; m < TPT; ++m) lds[TPT * tid + m] = e[m];
+    }
+    lds_barrier();
+    const int half = live >> 1;
+    if (TPT * tid < half) {
+#pragma unroll
+      for (int m = 0; m < TPT; ++m) {
+        const int i = TPT * tid + m;
+        const int r = i / P, o = i % P;         // survivor run r, offset o
+        const unsigned long long x = lds[2 * r * P + o], y = lds[(2 * r + 1) * P + o];
+        e[m] = x > y ? x : y;
+      }
+      for (int j = P >> 1; j > 0; j >>= 1) {    // sort each run: P / 2 .. 1
+        if (j < TPT) {                          // both elements in this thread
+#pragma unroll
+          for (int m = 0; m < TPT; ++m) {
+            const int mp = m ^ j;
+            if (mp > m) {
+              const int i = TPT * tid + m;
+              const bool desc = ((i / P) & 1) == 0;
+              const unsigned long long x = e[m], y = e[mp];
+              if (desc ? (x < y) : (x > y)) {
+                e[m] = y;
+                e[mp] = x;
+              }
+            }
+          }
+          continue;
+        }
+        const int tj = j / TPT;                 // partner thread in the wave
+        const bool lower = (tid & tj) == 0;
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) {
+          const unsigned long long y = shfl_xor64(e[m], tj);
+          const int i = TPT * tid + m;
+          const bool keep_max = (((i / P) & 1) == 0) == lower;
+          const unsigned long long x = e[m];
+          e[m] = keep_max ? (x > y ? x : y) : (x < y ? x : y);
+        }
+      }
+    }
+  }
+}
+
 // Code of channel cc of a 1/2-bit code dword as a float, from the dword
 // masked to one code per byte: mw[r] = (h >> (W * r)) & (one code mask in
 // each byte), so channel cc = (8 / W) * byte + r sits in byte cc / (8 / W)
@@ -144,8 +216,12 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
   constexpr int NGC = kChunk / 32 + 1;           // key groups a chunk can touch
   constexpr int SZR = D + 1;                     // padded row: groups in distinct banks
   __shared__ float s_q[D][GS];                   // q of the group, channel-major
-  __shared__ float2 s_sz[NGC * SZR];             // (s, z) of the chunk's key groups
-  __shared__ unsigned long long s_x[NT * TPT];   // cross-wave sort exchange
+  __shared__ __half2 s_sz[NGC * SZR];            // (s, z) of the chunk's key groups
+  // the selection's exchange buffer reuses the (s, z) rows: every LDS write
+  // of the selection follows a barrier after the last scoring read
+  static_assert(sizeof(__half2) * NGC * SZR >= sizeof(unsigned long long) * NT * TPT,
+                "exchange buffer fits the staged scales");
+  unsigned long long* s_x = (unsigned long long*)s_sz;
   const CacheGeom& g = a.g;
   const int b = blockIdx.z, kvh = blockIdx.y, chunk = blockIdx.x;
   const int tid = threadIdx.x;
@@ -163,9 +239,8 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
   const __half2* ksz = a.p.k_sz + blk * g.ksz_block;
   for (int e = tid; e < ng * D; e += NT) {
     const int gi = e / D, c = e % D;
-    s_sz[gi * SZR + c] = (gi0 + gi) * g.G < a.n_q
-                             ? __half22float2(ksz[(gi0 + gi) * D + c])
-                             : make_float2(0.f, 0.f);
+    s_sz[gi * SZR + c] = (gi0 + gi) * g.G < a.n_q ? ksz[(gi0 + gi) * D + c]
+                                                  : __floats2half2_rn(0.f, 0.f);
   }
   __syncthreads();
 
@@ -194,7 +269,7 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
           hw[m][4 * x] = v.x; hw[m][4 * x + 1] = v.y;
           hw[m][4 * x + 2] = v.z; hw[m][4 * x + 3] = v.w;
         }
-      const float2* sz = s_sz + (int)(j0 / g.G - gi0) * SZR;
+      const __half2* sz = s_sz + (int)(j0 / g.G - gi0) * SZR;
       float acc[TPT][GS];
 #pragma unroll
       for (int m = 0; m < TPT; ++m)
@@ -225,7 +300,7 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
 #pragma unroll
         for (int cc = 0; cc < CPD; ++cc) {
           const int c = x * CPD + cc;
-          const float2 p = sz[c];                // (s, z)
+          const float2 p = __half22float2(sz[c]);   // (s, z)
           float qc[GS];
 #pragma unroll
           for (int h = 0; h < GS; ++h) qc[h] = s_q[c][h];
@@ -269,7 +344,7 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
             lw[4 * x] = u.x; lw[4 * x + 1] = u.y; lw[4 * x + 2] = u.z; lw[4 * x + 3] = u.w;
           }
         }
-        const float2* sz = s_sz + (int)(j / g.G - gi0) * SZR;
+        const __half2* sz = s_sz + (int)(j / g.G - gi0) * SZR;
         float acc[GS];
 #pragma unroll
         for (int h = 0; h < GS; ++h) acc[h] = 0.f;
@@ -288,7 +363,7 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
           for (int cc = 0; cc < CPD; ++cc) {
             const int c = x * CPD + cc;
             const float code = code_of<BITS, PATH>(h0, l0, cc);
-            const float2 p = sz[c];                // (s, z)
+            const float2 p = __half22float2(sz[c]);   // (s, z)
             // z + code * s, code * s exact: one fused op rounds the same
             const float kc = __builtin_fmaf(code, p.x, p.y);
 #pragma unroll
@@ -305,7 +380,13 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
     }
   }
 
-  sort_regs_desc<NT>(comp, s_x);
+  // the chunk's best k, sorted descending: the top-P network for P the
+  // power of two at or above k, a full sort when P would exceed half the
+  // chunk
+  int P = TPT;
+  while (P < a.k) P <<= 1;
+  if (P <= NT * TPT / 2) chunk_top(comp, s_x, P);
+  else sort_regs_desc<NT>(comp, s_x);
   unsigned long long* cand = a.cand + (blk * a.chunks + chunk) * a.k;
 #pragma unroll
   for (int m = 0; m < TPT; ++m)
