@@ -17,11 +17,11 @@
 //     pairs staged in LDS; a token's sum runs over c = 0..d-1 in order.
 //     Each key becomes a 64-bit composite (order-preserving key bits << 32 |
 //     ~index), so one unsigned compare orders by key descending then index
-//     ascending.  The chunk is sorted by a bitonic network over the 4
-//     composites each thread holds in registers: compare partners in the
-//     same thread or wave are exchanged by lane shuffles, and only the 3
-//     stages whose partners sit in another wave go through LDS.  The
-//     chunk's best k go to the workspace.
+//     ascending.  The chunk's best P (the power of two at or above k) are
+//     selected by a bitonic top-P network over the 4 composites each thread
+//     holds in registers (compare partners in the same thread or wave are
+//     exchanged by lane shuffles; the halving levels pass the survivors
+//     through LDS), and its best k go to the workspace, sorted descending.
 //   merge_kernel, grid Hkv x B, 512 threads: sorts a block's chunk
 //     candidates with the same register network, 2048 at a time, and
 //     writes the best k.  The kernel boundary makes the candidates visible;
