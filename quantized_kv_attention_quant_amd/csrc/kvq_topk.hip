@@ -22,9 +22,9 @@
 //     holds in registers (compare partners in the same thread or wave are
 //     exchanged by lane shuffles; the halving levels pass the survivors
 //     through LDS), and its best k go to the workspace, sorted descending.
-//   merge_kernel, grid Hkv x B, 512 threads: sorts a block's chunk
-//     candidates with the same register network, 2048 at a time, and
-//     writes the best k.  The kernel boundary makes the candidates visible;
+//   merge_kernel, grid Hkv x B, 512 threads: the chunks' sorted candidate
+//     lists enter the same top-P levels as runs, 2048 elements at a time,
+//     and the best k are written.  The kernel boundary makes the candidates visible;
 //     no fence or counter is needed.
 #include "kvq_internal.h"
 
@@ -123,20 +123,20 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The best P of the workgroup's NT * 4 composites (P a power of two, 4 <= P
-// <= NT * 2), sorted descending into element 4 * tid + m of the first P / 4
-// threads.  The network sorts runs of P (alternately descending and
-// ascending), then halves the live elements level by level: the max of
-// element i of a descending run and element i of the ascending run after
-// it holds the best P of the two (a bitonic sequence), which log2(P)
-// compare-exchange stages sort again.  The survivors of each level move
-// through LDS to the first threads, so the waves left without live
-// elements drop out of the later levels.
-__device__ void chunk_top(unsigned long long (&e)[TPT], unsigned long long* lds,
-                          int P) {
+// Levels of a bitonic top-P network: from `live` composites (element
+// 4 * tid + m in e[m], runs of P alternately descending and ascending, P a
+// power of two, 4 <= P <= live / 2) down to the best P, sorted descending
+// in the first P / 4 threads.  Each level keeps the max of element i of a
+// descending run and element i of the ascending run after it (the best P
+// of the two, a bitonic sequence) and sorts it again in log2(P)
+// compare-exchange stages, alternating the direction by run.  The
+// survivors of each level move through LDS to the first threads, so the
+// waves left without live elements drop out of the later levels.
+template <int NTS>
+__device__ void top_reduce(unsigned long long (&e)[TPT], unsigned long long* lds,
+                           int P, int live) {
   const int tid = threadIdx.x;
-  sort_regs_desc<NT>(e, lds, 2, P);
-  for (int live = NT * TPT; live > P; live >>= 1) {
+  for (; live > P; live >>= 1) {
     lds_barrier();                              // earlier readers of lds done
     if (TPT * tid < live) {
 #pragma unroll
@@ -182,6 +182,15 @@ __device__ void chunk_top(unsigned long long (&e)[TPT], unsigned long long* lds,
       }
     }
   }
+}
+
+// The best P of the workgroup's NT * 4 composites, sorted descending in the
+// first P / 4 threads: runs of P sorted by the network's first stages, then
+// the halving levels.
+__device__ void chunk_top(unsigned long long (&e)[TPT], unsigned long long* lds,
+                          int P) {
+  sort_regs_desc<NT>(e, lds, 2, P);
+  top_reduce<NT>(e, lds, P, NT * TPT);
 }
 
 // Code of channel cc of a 1/2-bit code dword as a float, from the dword
@@ -393,8 +402,7 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
     if (TPT * tid + m < a.k) cand[TPT * tid + m] = comp[m];
 }
 
-// One workgroup per block: the best k of the chunks' candidates, sorted in
-// registers 2048 at a time (the best k stay in place, the rest refill).
+// One workgroup per block: the best k of the chunks' candidates.
 constexpr int NTM = 512;                 // merge threads
 __global__ void __launch_bounds__(NTM) merge_kernel(const TopkArgs a) {
   __shared__ unsigned long long s_x[NTM * TPT];
@@ -403,29 +411,32 @@ __global__ void __launch_bounds__(NTM) merge_kernel(const TopkArgs a) {
   const int tid = threadIdx.x;
   const int64_t blk = (int64_t)b * a.g.Hkv + kvh;
   const unsigned long long* all = a.cand + blk * a.chunks * a.k;
-  const int total = a.chunks * a.k;
   unsigned long long e[TPT];
-  // each chunk's k candidates are sorted descending; for k a power of two
-  // the chunk lists fill whole runs of the network, so loading every odd
-  // list reversed gives the state after its stages below 2k
-  const bool runs = (a.k & (a.k - 1)) == 0;
+  // each chunk's k candidates are sorted descending: chunk list c becomes a
+  // run of P (P the power of two at or above k; past k, zeros, below every
+  // real key), odd runs reversed, which is the state the top-P levels
+  // start from; cap / P runs per pass, the best run kept as run 0 of the
+  // next pass
+  int P = TPT;
+  while (P < a.k) P <<= 1;
+  const int R = cap / P;                        // runs per pass (>= 8)
+  auto elem = [&](int r, int c, int o) {        // run r from chunk c, offset o
+    const int x = (r & 1) ? P - 1 - o : o;
+    return c < a.chunks && x < a.k ? all[(int64_t)c * a.k + x] : 0ull;
+  };
 #pragma unroll
   for (int m = 0; m < TPT; ++m) {
     const int i = TPT * tid + m;
-    const int r = i / a.k, src = runs && (r & 1) ? r * a.k + (a.k - 1 - i % a.k) : i;
-    e[m] = i < total ? all[src] : 0ull;
+    e[m] = elem(i / P, i / P, i % P);
   }
-  sort_regs_desc<NTM>(e, s_x, runs ? 2 * a.k : 2);
-  for (int taken = cap; taken < total; taken += cap - a.k) {
+  top_reduce<NTM>(e, s_x, P, cap);
+  for (int next = R; next < a.chunks; next += R - 1) {
 #pragma unroll
     for (int m = 0; m < TPT; ++m) {
       const int i = TPT * tid + m;
-      if (i >= a.k) {
-        const int src = taken + i - a.k;
-        e[m] = src < total ? all[src] : 0ull;
-      }
+      if (i >= P) e[m] = elem(i / P, next + i / P - 1, i % P);
     }
-    sort_regs_desc<NTM>(e, s_x);
+    top_reduce<NTM>(e, s_x, P, cap);
   }
   int32_t* idx = a.idx + blk * a.k;
   float* key = a.key ? a.key + blk * a.k : nullptr;
@@ -470,7 +481,8 @@ hipError_t by_d(const TopkArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  if (a.chunk != kChunk || a.k > NT * TPT) return hipErrorInvalidValue;
+  // the top-P levels exchange compare partners within a wave: P <= 256
+  if (a.chunk != kChunk || a.k < 1 || a.k > 256) return hipErrorInvalidValue;
   if (a.g.bits == 8)
     return a.path == KVQ_DRAFT4 ? by_d<8, KVQ_DRAFT4>(a, s)
                                 : by_d<8, KVQ_TARGET>(a, s);
