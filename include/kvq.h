@@ -190,7 +190,10 @@ size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq);
  *   must be ordered (same stream).
  *   Range: value groups need scale s <= 63 (the PV step multiplies fp16
  *   probabilities scaled to at most 2^10 by s in fp16); every input finite.
- * Requires 1 <= T <= 16, T <= n_r, Hq % Hkv == 0, (Hq/Hkv)*T <= 32. */
+ *   Rows: one launch pair handles the T * Hq/Hkv query rows of a kv head
+ *   up to 32; above that, the query heads of each kv group run in
+ *   consecutive launch pairs of 32 / T heads (each reading the cache).
+ * Requires 1 <= T <= 16, T <= n_r, Hq % Hkv == 0. */
 int kv_attn_verify(const kvq_cache* c, const void* q, int T, int Hq, int path,
                    float sm_scale, void* out, float* lse, void* ws,
                    size_t ws_bytes, void* stream);

@@ -206,9 +206,6 @@ int attn_setup(const kvq_cache* c, const void* q, int T, int Hq, int path,
     return fail(KVQ_EINVAL, "T = %d exceeds the %lld residual tokens", T,
                 (long long)c->n_r);
   if (Hq < 1 || Hq % c->Hkv) return fail(KVQ_EINVAL, "Hq must be a multiple of Hkv");
-  if (T * (Hq / c->Hkv) > 32)
-    return fail(KVQ_EUNSUPPORTED, "T * Hq/Hkv = %d rows exceeds 32",
-                T * (Hq / c->Hkv));
   if (path != KVQ_TARGET && path != KVQ_DRAFT4)
     return fail(KVQ_EINVAL, "unknown path %d", path);
   if (path == KVQ_DRAFT4 && c->bits != 8)
@@ -229,7 +226,9 @@ int attn_setup(const kvq_cache* c, const void* q, int T, int Hq, int path,
   a.T = T;
   a.Hq = Hq;
   a.gs = Hq / c->Hkv;
-  a.rows = T * a.gs;
+  a.h0 = 0;
+  a.hs = a.gs;
+  a.rows = T * a.gs;   // above 32, launch_attn splits the heads
   a.path = path;
   a.c0 = sm_scale * 1.4426950408889634f;
   a.S = 0;

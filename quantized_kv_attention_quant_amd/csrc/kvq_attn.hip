@@ -378,7 +378,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
     o += *(const f4v*)(src + sp * pstride) * sw[sp];
   part[pg][cq] = o;
   __syncthreads();
-  const int t = row / a.gs, h = kvh * a.gs + row % a.gs;
+  const int t = row / a.hs, h = kvh * a.gs + a.h0 + row % a.hs;
   if (pg == 0) {
     f4v tot = part[0][cq];
 #pragma unroll
@@ -445,7 +445,7 @@ __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
   __shared__ float s_o[NWV][HB][D], s_m[NWV][HB], s_l[NWV][HB];
   const CacheGeom& g = a.g;
   const int hl0 = blockIdx.x * HB, kvh = blockIdx.y, b = blockIdx.z;
-  const int nh = a.gs - hl0 < HB ? a.gs - hl0 : HB;   // heads of this workgroup
+  const int nh = a.hs - hl0 < HB ? a.hs - hl0 : HB;   // heads of this workgroup
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = a.n_exact;
@@ -459,7 +459,7 @@ __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
   for (int t = 0; t < a.T; ++t) {
     if (t == a.t_exact) continue;
     for (int hh = 0; hh < nh; ++hh) {
-      const int r = t * a.gs + hl0 + hh;
+      const int r = t * a.hs + hl0 + hh;
       for (int c = tid; c < D; c += NT) po[r * D + c] = 0.f;
       if (tid == 0) {
         po[RP * D + r] = -INFINITY;
@@ -470,7 +470,7 @@ __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
   for (int e = tid; e < HB * D; e += NT) {
     const int hh = e / D, c = e % D;
     s_q[hh][c] = hh < nh ? __half2float(a.q[(((int64_t)b * a.T + a.t_exact) * a.Hq +
-                                             kvh * a.gs + hl0 + hh) * D + c]) * a.c0
+                                             kvh * a.gs + a.h0 + hl0 + hh) * D + c]) * a.c0
                          : 0.f;
   }
   __syncthreads();
@@ -547,7 +547,7 @@ __global__ void __launch_bounds__(512, 2) exact_kernel(const AttnArgs a) {
       ot += s_o[w][hh][c] * sc;
       lt += s_l[w][hh] * sc;
     }
-    const int row = a.t_exact * a.gs + hl0 + hh;
+    const int row = a.t_exact * a.hs + hl0 + hh;
     po[row * D + c] = ot;
     if (c == 0) {
       po[RP * D + row] = M;
@@ -778,7 +778,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
       qv[i] = u4v{0u, 0u, 0u, 0u};
       if (k < q_chunks) {
         const int r = k / (D / 8), c8 = k % (D / 8);
-        const int t = r / a.gs, hl = r % a.gs;
+        const int t = r / a.hs, hl = a.h0 + r % a.hs;
         qv[i] = *(const u4v*)(a.q + (((int64_t)b * a.T + t) * a.Hq + kvh * a.gs + hl) * D +
                               8 * c8);
       }
@@ -814,7 +814,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   }
   int cur_grp = -2;                    // -1: ring operands, >= 0: key group
   // exact substitution: rows of query token t_exact (one per GQA head)
-  const int xlo = a.t_exact * a.gs, xhi = xlo + a.gs;
+  const int xlo = a.t_exact * a.hs, xhi = xlo + a.hs;
   const DecK dk = dec_consts();
   const float c0 = a.c0;
   // channels this lane multiplies in key-group operands: (cA(ks) + j,
@@ -1149,7 +1149,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       const int row = row_of(rt);
-      const int lim = row < a.rows ? L - a.T + row / a.gs : L - 1;
+      const int lim = row < a.rows ? L - a.T + row / a.hs : L - 1;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -1381,7 +1381,7 @@ hipError_t go(AttnArgs a, hipStream_t s) {
       e = hipStreamWaitEvent(s, (hipEvent_t)a.rows_ready, 0);
       if (e != hipSuccess) return e;
     }
-    const dim3 xg((unsigned)cdiv(a.gs, 4), (unsigned)a.g.Hkv, (unsigned)a.g.B);
+    const dim3 xg((unsigned)cdiv(a.hs, 4), (unsigned)a.g.Hkv, (unsigned)a.g.B);
     hipLaunchKernelGGL((exact_kernel<D, C::RP>), xg, dim3(512), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1456,7 +1456,8 @@ hipError_t attn_scratch(void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+namespace {
+hipError_t launch_rows(const AttnArgs& a, hipStream_t s) {
   const int bits = a.g.bits, d = a.g.d;
   if (bits == 8 && a.path == KVQ_DRAFT4)
     return d == 64 ? by_rows<P_D4, 64>(a, s) : by_rows<P_D4, 128>(a, s);
@@ -1466,6 +1467,26 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     return d == 64 ? by_rows<P_L2, 64>(a, s) : by_rows<P_L2, 128>(a, s);
   if (bits == 1 && d == 128) return by_rows<P_L1, 128>(a, s);
   return hipErrorInvalidValue;
+}
+}  // namespace
+
+// Calls with more than 32 rows (T * Hq/Hkv) run as consecutive launches over
+// subsets of each kv group's query heads, hs = 32 / T heads at a time: every
+// launch reads the whole cache for its heads and writes their rows of out
+// and lse; the partial slots are reused in stream order.
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+  if (a.rows <= 32) return launch_rows(a, s);
+  const int hs = 32 / a.T;
+  for (int h0 = 0; h0 < a.gs; h0 += hs) {
+    AttnArgs b = a;
+    b.h0 = h0;
+    b.hs = a.gs - h0 < hs ? a.gs - h0 : hs;
+    b.rows = a.T * b.hs;
+    b.rows_pad = b.rows <= 16 ? 16 : 32;
+    const hipError_t e = launch_rows(b, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kvq

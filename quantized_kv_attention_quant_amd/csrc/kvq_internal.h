@@ -160,6 +160,8 @@ struct AttnArgs {
   float* ws;        // partials: [B*Hkv][s_alloc][rows_pad][d + 2] float
   int64_t n_q, n_r;
   int T, Hq, gs, rows;
+  int h0, hs;       // this launch's query heads of each kv group: h0 .. h0+hs-1
+                    // (rows = T * hs; all gs heads unless rows would pass 32)
   int path;         // KVQ_TARGET / KVQ_DRAFT4
   float c0;         // sm_scale * log2(e)
   int S;            // split workgroups per block (set by the launcher)

@@ -158,7 +158,6 @@ def test_verify_errors_before_launch():
         c, FakeT(), T, Hq, path, 0.088, FakeT(), None, ws, 0)
     assert _code(lambda: call(T=0)) == kq.KVQ_EINVAL
     assert _code(lambda: call(T=17)) == kq.KVQ_EINVAL
-    assert _code(lambda: call(T=9, Hq=32)) == kq.KVQ_EUNSUPPORTED  # 36 rows
     assert _code(lambda: call(Hq=30)) == kq.KVQ_EINVAL
     assert _code(lambda: call(path=5)) == kq.KVQ_EINVAL
     assert _code(lambda: call(ws=FakeT(ws.n - 1))) == kq.KVQ_EWORKSPACE

@@ -31,6 +31,9 @@ CASES = [
     # T = 16: the substituted row is the last of 32 rows, or a middle one
     ("gqa2_t16_last", W("gqa2", 1, 4, 2, 128, 900, 64, 64, 128, 8, "outlier"),
      "target", 16, 15),
+    # 8 query heads per kv head at T = 6: 48 rows, run as two head subsets
+    ("gqa8_t6", W("gqa8", 1, 16, 2, 128, 1500, 64, 64, 128, 8, "outlier"),
+     "target", 6, 4),
     ("mha_d64_t16_draft", W("mha_d64_int8", 1, 3, 3, 64, 777, 64, 32, 128, 8,
                             "outlier"), "draft4", 16, 7),
 ]

@@ -46,6 +46,8 @@ SMALL = {
     "g256": W("g256", 1, 4, 2, 128, 1800, 256, 64, 256, 8, "outlier"),
     "d64_g256_2bit": W("d64_g256_2bit", 1, 4, 2, 64, 1500, 256, 32, 256, 2,
                        "normal"),
+    # 8 query heads per kv head: T * 8 rows above 32 run as head subsets
+    "gqa8": W("gqa8", 1, 16, 2, 128, 1500, 64, 64, 128, 8, "outlier"),
 }
 
 
@@ -128,7 +130,9 @@ RUNS = [("tiny", "target", 1), ("tiny", "draft4", 1), ("tiny", "target", 8),
         ("mha_d64_int8", "target", 16), ("gqa2", "target", 16),
         ("gqa2", "draft4", 16),
         ("g256", "target", 5), ("g256", "draft4", 1),
-        ("d64_g256_2bit", "target", 3)]
+        ("d64_g256_2bit", "target", 3),
+        # 40 rows (heads 0-5, then 6-7), 64 rows (2 x 4 heads), 128 rows
+        ("gqa8", "target", 5), ("gqa8", "target", 8), ("gqa8", "draft4", 16)]
 
 
 @pytest.mark.parametrize("name,path,T", RUNS)
