@@ -32,8 +32,11 @@
  *
  * Conventions for every call
  *   - Ownership: the caller owns every buffer (host struct and device
- *     memory).  The library never allocates or frees memory and keeps no
- *     global state except the thread-local message of kv_last_error.
+ *     memory).  The library never allocates or frees memory.  Its only
+ *     global state is the thread-local message of kv_last_error and, for
+ *     kv_attn_verify_noalloc, a static device array on each GPU (32 MiB,
+ *     held until the process ends) with its address looked up once per
+ *     device.
  *   - Pointers named "device" are HIP device addresses; `stream` is a
  *     hipStream_t handle (NULL = the null stream).  All device work is
  *     enqueued on `stream` and is asynchronous to the host.
@@ -265,7 +268,8 @@ size_t kv_topk_workspace_bytes(const kvq_cache* c, int Hq, int k);
  * ws: >= kv_topk_workspace_bytes(c, Hq, k) bytes; it needs no initial
  * contents and holds the per-chunk candidates between the call's two
  * launches (scoring, then merge).  Calls sharing one ws must be ordered
- * (same stream).  Requires 1 <= k <= 256, Hq % Hkv == 0, Hq/Hkv <= 8. */
+ * (same stream).  Requires 1 <= k <= 256, Hq % Hkv == 0, Hq/Hkv in
+ * {1, 2, 4, 8}. */
 int kv_topk(const kvq_cache* c, const void* q_spec, int Hq, int path, int k,
             int32_t* idx, float* key, void* ws, size_t ws_bytes, void* stream);
 
