@@ -1,8 +1,8 @@
 """kv_attn_verify_noalloc: the attention entry point for callers that cannot
 allocate (its partials live in a static device scratch) against the
-workspace entry point kv_attn_verify on the same caches and queries, two
-calls in a row with the second on a smaller input, plus its size limit
-(checked before any HIP call)."""
+workspace entry point kv_attn_verify on the same caches and queries, three
+calls in a row, each on a smaller input than the one before, plus its size
+limit (checked before any HIP call)."""
 import numpy as np
 import pytest
 import torch
@@ -15,10 +15,14 @@ from kvq_testlib import (assert_attn_close, host_tokens, say, shape_for,
 
 W = synth.Workload
 
-# a GQA INT8 verify over several splits, then a smaller MHA-group draft
+# a GQA INT8 verify over several splits, then a smaller one with 8 query
+# heads per kv head (48 rows: two launch pairs over head subsets), then a
+# smaller MHA-group draft
 CASES = [
     ("gqa_int8_t7", W("gqa_int8_t7", 2, 8, 2, 128, 3000, 128, 64, 256, 8,
                       "outlier_drift"), 7, "target"),
+    ("gqa8_int8_t6", W("gqa8_int8_t6", 1, 16, 2, 128, 1500, 64, 64, 128, 8,
+                       "outlier"), 6, "target"),
     ("tiny_draft_t1", synth.WORKLOADS["tiny"], 1, "draft4"),
 ]
 
