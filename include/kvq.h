@@ -268,8 +268,7 @@ size_t kv_topk_workspace_bytes(const kvq_cache* c, int Hq, int k);
  * ws: >= kv_topk_workspace_bytes(c, Hq, k) bytes; it needs no initial
  * contents and holds the per-chunk candidates between the call's two
  * launches (scoring, then merge).  Calls sharing one ws must be ordered
- * (same stream).  Requires 1 <= k <= 256, Hq % Hkv == 0, Hq/Hkv in
- * {1, 2, 4, 8}. */
+ * (same stream).  Requires 1 <= k <= 256, Hq % Hkv == 0, Hq/Hkv <= 8. */
 int kv_topk(const kvq_cache* c, const void* q_spec, int Hq, int path, int k,
             int32_t* idx, float* key, void* ws, size_t ws_bytes, void* stream);
 

@@ -324,8 +324,7 @@ KVQ_API int kv_topk(const kvq_cache* c, const void* q_spec, int Hq, int path,
   if (k < 1 || k > kMaxTopk) return fail(KVQ_EINVAL, "k must be in [1, 256]");
   if (Hq < 1 || Hq % c->Hkv) return fail(KVQ_EINVAL, "Hq must be a multiple of Hkv");
   const int gs = Hq / c->Hkv;
-  if (gs != 1 && gs != 2 && gs != 4 && gs != 8)
-    return fail(KVQ_EUNSUPPORTED, "Hq/Hkv must be 1, 2, 4 or 8");
+  if (gs > 8) return fail(KVQ_EUNSUPPORTED, "Hq/Hkv must be at most 8");
   if (path != KVQ_TARGET && path != KVQ_DRAFT4)
     return fail(KVQ_EINVAL, "unknown path %d", path);
   if (path == KVQ_DRAFT4 && c->bits != 8)

@@ -236,9 +236,12 @@ __global__ void __launch_bounds__(NT) score_kernel(const TopkArgs a) {
   const int tid = threadIdx.x;
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
 
+  // GS is a.gs rounded up to a power of two; the slots past a.gs repeat
+  // the group's last head, whose logit the max already holds
   for (int e = tid; e < GS * D; e += NT) {
     const int h = e / D, c = e % D;
-    s_q[c][h] = __half2float(a.q[((int64_t)b * a.Hq + kvh * GS + h) * D + c]);
+    const int hs = h < a.gs ? h : a.gs - 1;
+    s_q[c][h] = __half2float(a.q[((int64_t)b * a.Hq + kvh * a.gs + hs) * D + c]);
   }
   // the key groups the chunk's tokens fall in (G is a multiple of 32, so a
   // chunk touches at most 1024/32 + 1); groups past n_q are not read
@@ -462,15 +465,14 @@ hipError_t go(const TopkArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Query heads per kv head, rounded up to a power of two (at most 8).
 template <int BITS, int PATH, int D>
 hipError_t by_gs(const TopkArgs& a, hipStream_t s) {
-  switch (a.gs) {
-    case 1: return go<BITS, PATH, D, 1>(a, s);
-    case 2: return go<BITS, PATH, D, 2>(a, s);
-    case 4: return go<BITS, PATH, D, 4>(a, s);
-    case 8: return go<BITS, PATH, D, 8>(a, s);
-    default: return hipErrorInvalidValue;
-  }
+  if (a.gs == 1) return go<BITS, PATH, D, 1>(a, s);
+  if (a.gs == 2) return go<BITS, PATH, D, 2>(a, s);
+  if (a.gs <= 4) return go<BITS, PATH, D, 4>(a, s);
+  if (a.gs <= 8) return go<BITS, PATH, D, 8>(a, s);
+  return hipErrorInvalidValue;
 }
 
 template <int BITS, int PATH>

@@ -175,7 +175,7 @@ def test_topk_errors_before_launch():
         c, FakeT(), Hq, path, k, FakeT(), None, ws, 0)
     assert _code(lambda: call(k=0)) == kq.KVQ_EINVAL
     assert _code(lambda: call(k=257)) == kq.KVQ_EINVAL
-    assert _code(lambda: call(Hq=24)) == kq.KVQ_EUNSUPPORTED     # gs = 3
+    assert _code(lambda: call(Hq=72)) == kq.KVQ_EUNSUPPORTED     # gs = 9
     assert _code(lambda: call(ws=FakeT(8))) == kq.KVQ_EWORKSPACE
     low = _fake_cache(bits=1, G=32, Gv=32, R=32, n_q=1024, n_r=8)
     assert _code(lambda: call(c=low, path=kq.KVQ_DRAFT4)) == kq.KVQ_EINVAL

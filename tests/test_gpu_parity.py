@@ -48,6 +48,9 @@ SMALL = {
                        "normal"),
     # 8 query heads per kv head: T * 8 rows above 32 run as head subsets
     "gqa8": W("gqa8", 1, 16, 2, 128, 1500, 64, 64, 128, 8, "outlier"),
+    # group sizes that are not powers of two (top-k pads them to 4 and 8)
+    "gqa3_2bit": W("gqa3_2bit", 1, 6, 2, 128, 2000, 32, 32, 32, 2, "normal"),
+    "gqa7": W("gqa7", 1, 14, 2, 128, 1500, 64, 64, 128, 8, "outlier"),
 }
 
 
@@ -132,7 +135,8 @@ RUNS = [("tiny", "target", 1), ("tiny", "draft4", 1), ("tiny", "target", 8),
         ("g256", "target", 5), ("g256", "draft4", 1),
         ("d64_g256_2bit", "target", 3),
         # 40 rows (heads 0-5, then 6-7), 64 rows (2 x 4 heads), 128 rows
-        ("gqa8", "target", 5), ("gqa8", "target", 8), ("gqa8", "draft4", 16)]
+        ("gqa8", "target", 5), ("gqa8", "target", 8), ("gqa8", "draft4", 16),
+        ("gqa3_2bit", "target", 2), ("gqa7", "target", 4)]
 
 
 @pytest.mark.parametrize("name,path,T", RUNS)
@@ -206,7 +210,9 @@ def test_verify_row_equals_prefix_decode():
     ("mha_d64_int8", "target", 256), ("tiny", "target", 300 // 2),
     ("g96", "target", 64), ("g96", "draft4", 64), ("g96_2bit", "target", 200),
     ("g32_bulk", "target", 128), ("long_2bit", "target", 256),
-    ("g256", "target", 64), ("d64_g256_2bit", "target", 32)])
+    ("g256", "target", 64), ("d64_g256_2bit", "target", 32),
+    ("gqa3_2bit", "target", 64), ("gqa7", "target", 100),
+    ("gqa7", "draft4", 64)])
 def test_topk_bit_exact(name, path, k):
     w = SMALL[name]
     say(f"[gpu] topk {name} {path} k={k}")
