@@ -270,6 +270,20 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The value of lane l ^ M (M = 1, 2 or 8) of this wave: one DPP move
+// (quad permutations for 1 and 2, a rotation by 8 within each 16-lane row).
+template <int M>
+__device__ __forceinline__ unsigned lane_xor(unsigned v) {
+  static_assert(M == 1 || M == 2 || M == 8, "DPP lane xor");
+  constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : 0x128;
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
+}
+// v OR-ed with the value of lane l ^ 16 (the 16-lane rows swapped).
+__device__ __forceinline__ unsigned lane_xor16(unsigned v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return s[0] | s[1];
+}
+
 // V-tile items: `count` consecutive 32-token tiles from tile `first`, 8
 // threads per token; thread (j, u) holds the CPV = D/8 channels u*CPV.. of
 // token j, a value group spans Gv/CPV threads whose min/max meet by lane
@@ -287,6 +301,10 @@ __device__ __forceinline__ void value_tiles(const AppendArgs& a, int first,
   constexpr int NL = CPV / 8;              // 16-byte row pieces per thread
   constexpr int WORDS = D * W;             // dwords per plane tile
   constexpr int PER = 4 / W;               // 16-channel groups per dword
+  // lane xor that steps m % PER (m = c / 16): u for head dim 128, u / 2 for 64
+  constexpr int MX1 = D == 128 ? 1 : 2;
+  static_assert(PER < 4 || D == 128, "1-bit codes need head dim 128");
+  constexpr bool FULL = W == 1;            // whole halves by one lane, no atomics
   const int ng = D / g.Gv;
   const int tpg = g.Gv / CPV;              // threads per value group (1..8)
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
@@ -325,9 +343,11 @@ __device__ __forceinline__ void value_tiles(const AppendArgs& a, int first,
     const int64_t tile = a.q0 / kTile + tl;  // q0 is a multiple of G
     if (k + 1 < count) load(tl + 1, nxt);
     if (k > 0) lds_barrier();              // the last tile's words read out
-    for (int w = threadIdx.x; w < WORDS; w += kThreads) {
-      lds_hi[w] = 0u;
-      if constexpr (BITS == 8) lds_lo[w] = 0u;
+    if constexpr (!FULL) {                 // atomics OR into cleared words
+      for (int w = threadIdx.x; w < WORDS; w += kThreads) {
+        lds_hi[w] = 0u;
+        if constexpr (BITS == 8) lds_lo[w] = 0u;
+      }
     }
     // group min/max: packed fp16 (exact), then across the group's lanes
     hv2 m2 = __builtin_bit_cast(hv2, cur[0].x), x2 = m2;
@@ -354,20 +374,39 @@ __device__ __forceinline__ void value_tiles(const AppendArgs& a, int first,
       sz[at] = __float2half_rn(sc);
       sz[32 * ng + at] = __float2half_rn(z);
     }
-    lds_barrier();                           // LDS words cleared
+    // Each half (h) of a tile dword holds the codes of the 4 tokens i of one
+    // (g, h) and the PER channel groups m % PER of one channel r: lanes of
+    // this wave that differ in i (lane bits 3-4) and in m % PER (lane bits
+    // from MX1).  With 1-bit codes (16 lanes per half) the contributions are
+    // OR-ed across those lanes and one lane writes the whole half, so no
+    // word needs clearing or an atomic update; with 2-bit codes they are
+    // OR-ed across m % PER and the 4 lanes left OR theirs into the cleared
+    // word; 8-bit codes go to LDS by atomic OR directly (4 lanes per word:
+    // there the lane moves cost more than the atomics' conflicts).
+    if constexpr (!FULL) lds_barrier();    // cleared words for the atomics
     const __half* hx = (const __half*)cur;
+    const bool lead_m = PER == 1 || (threadIdx.x & (MX1 * (PER - 1))) == 0;
 #pragma unroll
     for (int k2 = 0; k2 < CPV; ++k2) {
       const int c = c0 + k2;
       const unsigned q = code_word(__half2float(hx[k2]), z, sc, rs, (float)Lv) & 255u;
       const int r = c & 15, m = c >> 4;
       const int dw = (16 * gg + r) * (D * W / 64) + m / PER;
-      const int bit = 16 * h + W * (4 * (m % PER) + i);
+      const int pos = W * (4 * (m % PER) + i);
       if constexpr (BITS == 8) {
-        atomicOr(&lds_hi[dw], (q >> 4) << bit);
-        atomicOr(&lds_lo[dw], (q & 15u) << bit);
+        atomicOr(&lds_hi[dw], (q >> 4) << (16 * h + pos));
+        atomicOr(&lds_lo[dw], (q & 15u) << (16 * h + pos));
       } else {
-        atomicOr(&lds_hi[dw], q << bit);
+        unsigned v = q << pos;
+        if constexpr (PER >= 2) v |= lane_xor<MX1>(v);
+        if constexpr (PER == 4) v |= lane_xor<2 * MX1>(v);
+        if constexpr (FULL) {
+          v |= lane_xor<8>(v);
+          v |= lane_xor16(v);
+          if (i == 0 && lead_m) ((unsigned short*)lds_hi)[2 * dw + h] = (unsigned short)v;
+        } else if (lead_m) {
+          atomicOr(&lds_hi[dw], v << (16 * h));
+        }
       }
     }
     lds_barrier();                           // the tile's words complete
