@@ -308,7 +308,15 @@ __device__ __forceinline__ void value_tiles(const AppendArgs& a, int first,
   const int ng = D / g.Gv;
   const int tpg = g.Gv / CPV;              // threads per value group (1..8)
   const int64_t blk = (int64_t)b * g.Hkv + kvh;
-  const int j = threadIdx.x / 8, u = threadIdx.x % 8;
+  // thread (j, u): token j, channels u*CPV..  For 8-bit codes wave w takes
+  // the tokens j = 4n + w (one i = j % 4 per wave), so the lanes of one LDS
+  // atomic meet in a word at most two at a time (h = 0, 1); otherwise a
+  // wave takes 8 consecutive tokens, which puts the 4 i of a word in one
+  // wave (for 1/2-bit codes the lane combining below relies on that, and
+  // it measured faster for 2-bit codes)
+  const int u = threadIdx.x % 8;
+  const int j = BITS != 8 ? threadIdx.x / 8
+                          : 4 * ((threadIdx.x % kWave) / 8) + threadIdx.x / kWave;
   const int c0 = u * CPV, grp = c0 / g.Gv;
   const int gg = (j & 15) >> 2, i = j & 3, h = j >> 4;
   // fp16 channels c0.. of token j of tile tl (appended rows: 16-byte
@@ -442,6 +450,10 @@ __device__ __forceinline__ void ring_token(const AppendArgs& a, int item, int b,
   }
 }
 
+// One kernel per (head dim, code width, key groups per item): a launch runs
+// only its own item code (a single kernel holding every instantiation
+// measured slower on the low-bit fills).
+template <int D, int W, int NGI>
 __global__ void __launch_bounds__(kThreads)
 append_kernel(AppendArgs a, Item it) {
   __shared__ unsigned lds_hi[128 * 4];
@@ -451,39 +463,14 @@ append_kernel(AppendArgs a, Item it) {
   const int b = blockIdx.z, kvh = blockIdx.y;
   int x = blockIdx.x;
   if (x < it.k_items) {
-    if (a.g.d == 128) {
-      const int ngi = kgroups_per_item(128, a.g.G);
-      if (ngi == 4) {
-        if (a.g.w == 4) key_group<128, 4, 4>(a, x, b, kvh, s_mn, s_mx);
-        else if (a.g.w == 2) key_group<128, 2, 4>(a, x, b, kvh, s_mn, s_mx);
-        else key_group<128, 1, 4>(a, x, b, kvh, s_mn, s_mx);
-      } else if (ngi == 2) {
-        if (a.g.w == 4) key_group<128, 4, 2>(a, x, b, kvh, s_mn, s_mx);
-        else if (a.g.w == 2) key_group<128, 2, 2>(a, x, b, kvh, s_mn, s_mx);
-        else key_group<128, 1, 2>(a, x, b, kvh, s_mn, s_mx);
-      } else {
-        if (a.g.w == 4) key_group<128, 4, 1>(a, x, b, kvh, s_mn, s_mx);
-        else if (a.g.w == 2) key_group<128, 2, 1>(a, x, b, kvh, s_mn, s_mx);
-        else key_group<128, 1, 1>(a, x, b, kvh, s_mn, s_mx);
-      }
-    } else {   // d = 64: 8-bit or 2-bit codes, one group per item
-      if (a.g.w == 4) key_group<64, 4, 1>(a, x, b, kvh, s_mn, s_mx);
-      else key_group<64, 2, 1>(a, x, b, kvh, s_mn, s_mx);
-    }
+    key_group<D, W, NGI>(a, x, b, kvh, s_mn, s_mx);
     return;
   }
   x -= it.k_items;
   if (x < it.v_items) {
     const int first = x * it.vt;
     const int count = min(it.vt, it.v_tiles - first);
-    if (a.g.d == 128) {
-      if (a.g.w == 4) value_tiles<128, 4>(a, first, count, b, kvh, lds_hi, lds_lo);
-      else if (a.g.w == 2) value_tiles<128, 2>(a, first, count, b, kvh, lds_hi, lds_lo);
-      else value_tiles<128, 1>(a, first, count, b, kvh, lds_hi, lds_lo);
-    } else {   // d = 64: 8-bit or 2-bit codes
-      if (a.g.w == 4) value_tiles<64, 4>(a, first, count, b, kvh, lds_hi, lds_lo);
-      else value_tiles<64, 2>(a, first, count, b, kvh, lds_hi, lds_lo);
-    }
+    value_tiles<D, W>(a, first, count, b, kvh, lds_hi, lds_lo);
     return;
   }
   x -= it.v_items;
@@ -496,12 +483,19 @@ append_kernel(AppendArgs a, Item it) {
   }
 }
 
+template <int D, int W, int NGI>
+hipError_t go(const AppendArgs& a, const Item& it, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((append_kernel<D, W, NGI>), grid, dim3(kThreads), 0, s, a, it);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_append(const AppendArgs& a, bool flush, bool ring_write,
                          hipStream_t s) {
   Item it;
-  it.k_items = flush ? (int)cdiv(a.groups, kgroups_per_item(a.g.d, a.g.G)) : 0;
+  const int ngi = kgroups_per_item(a.g.d, a.g.G);
+  it.k_items = flush ? (int)cdiv(a.groups, ngi) : 0;
   it.v_tiles = flush ? (int)((int64_t)a.groups * a.g.G / kTile) : 0;
   it.r_tokens = ring_write ? a.wr_count : 0;
   it.vt = it.v_tiles >= 64 ? 4 : 1;
@@ -510,9 +504,27 @@ hipError_t launch_append(const AppendArgs& a, bool flush, bool ring_write,
   it.ring_items = (int)cdiv(it.r_tokens, it.rt);
   const int64_t nx = (int64_t)it.k_items + it.v_items + it.ring_items;
   if (nx == 0) return hipSuccess;
-  dim3 grid((unsigned)nx, a.g.Hkv, a.g.B);
-  hipLaunchKernelGGL(append_kernel, grid, dim3(kThreads), 0, s, a, it);
-  return hipGetLastError();
+  const dim3 grid((unsigned)nx, a.g.Hkv, a.g.B);
+  const int w = a.g.w;
+  if (a.g.d == 64) {                  // 8-bit or 2-bit codes, one group per item
+    if (w == 4) return go<64, 4, 1>(a, it, grid, s);
+    if (w == 2) return go<64, 2, 1>(a, it, grid, s);
+    return hipErrorInvalidValue;
+  }
+  if (a.g.d != 128) return hipErrorInvalidValue;
+  if (ngi == 4) {
+    if (w == 4) return go<128, 4, 4>(a, it, grid, s);
+    if (w == 2) return go<128, 2, 4>(a, it, grid, s);
+    return go<128, 1, 4>(a, it, grid, s);
+  }
+  if (ngi == 2) {
+    if (w == 4) return go<128, 4, 2>(a, it, grid, s);
+    if (w == 2) return go<128, 2, 2>(a, it, grid, s);
+    return go<128, 1, 2>(a, it, grid, s);
+  }
+  if (w == 4) return go<128, 4, 1>(a, it, grid, s);
+  if (w == 2) return go<128, 2, 1>(a, it, grid, s);
+  return go<128, 1, 1>(a, it, grid, s);
 }
 
 }  // namespace kvq
