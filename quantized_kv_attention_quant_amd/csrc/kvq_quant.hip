@@ -452,9 +452,13 @@ __device__ __forceinline__ void ring_token(const AppendArgs& a, int item, int b,
 
 // One kernel per (head dim, code width, key groups per item): a launch runs
 // only its own item code (a single kernel holding every instantiation
-// measured slower on the low-bit fills).
+// measured slower on the low-bit fills).  The 8-bit kernels are held to 96
+// VGPRs for five waves per SIMD (117 and four waves unconstrained): the
+// ~24 registers spilled cost less than the fifth wave gains (32K prefill
+// 54.0 against 56.1 us); the low-bit kernels (107-108 VGPRs) keep four.
 template <int D, int W, int NGI>
 __global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(W == 4 ? 5 : 4)))
 append_kernel(AppendArgs a, Item it) {
   __shared__ unsigned lds_hi[128 * 4];
   __shared__ unsigned lds_lo[128 * 4];
