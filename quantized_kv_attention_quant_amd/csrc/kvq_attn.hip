@@ -31,7 +31,11 @@
 //     Q' = q * s * sm_scale * log2(e) once per key group, kept as two fp16
 //     parts (hi + lo, two MFMAs) so the scores carry ~22 bits of Q'; the 1024
 //     offset (an MFMA of a constant operand with Q') and the zero-points go
-//     into the accumulator's initial value.  Per-token value scales are
+//     into the accumulator's initial value.  1/2-bit caches (groups of 32
+//     tokens) cut that per-group work: 1-bit codes carry their key scales
+//     themselves (code s / 2 is exact), 2-bit groups rebuild Q' with packed
+//     fp16 operations from fixed hi + lo parts of q * c0, and both take the
+//     zero-point term as one MFMA.  Per-token value scales are
 //     folded into P' = p * s * 2^7, value zero-points and the 1024 offset
 //     into a per-row fp32 side sum (packed fp16 dot products).
 //   * the softmax reference moves lazily: scores are taken relative to the
@@ -230,6 +234,21 @@ template <int W>
 __device__ __forceinline__ unsigned declow(unsigned H, int i, const DecK& k) {
   constexpr unsigned mask = ((1u << W) - 1u) * 0x00010001u;
   return hadd2(((H >> (W * i)) & mask) | k.magic, kMinus1024);
+}
+
+// W-bit key codes times their channels' key scales: the pair at bits
+// (W*i, 16 + W*i) goes under the fp16 exponent of 1.0 as the top mantissa
+// bits, x = 1 + code 2^-W (exact), and fma(x, s, -s) = code s 2^-W with a
+// single rounding (x s < 2 s: no overflow).  `one` is the fp16 pair
+// (1, 1), `m` the code bits' mask at their place under it.
+template <int W>
+__device__ __forceinline__ unsigned declow_ks(unsigned H, int i, unsigned s,
+                                              unsigned one, unsigned m) {
+  const int sh = (10 - W) - W * i;   // a constant once the caller unrolls
+  const unsigned x = sh >= 0 ? H << (sh & 31) : H >> (-sh & 31);
+  const h2v xv = __builtin_bit_cast(h2v, (x & m) | one);
+  const h2v sv = __builtin_bit_cast(h2v, s);
+  return __builtin_bit_cast(unsigned, __builtin_elementwise_fma(xv, sv, -sv));
 }
 
 template <int N>
@@ -827,8 +846,9 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   constexpr int DAB = C::W == 4 ? 4 : C::W == 2 ? 8 : 16;   // cB - cA
   // With one row tile, q * c0 of those channels stays in registers for the
   // whole run (measured faster than re-reading it from LDS per key group);
-  // with two it is re-read (registers).
-  constexpr bool QC = NRT == 1;
+  // with two it is re-read (registers).  1/2-bit codes carry their key
+  // scales themselves and never rebuild Q'.
+  constexpr bool QC = NRT == 1 && !C::LOW;
   float qcA[QC ? KS : 1][4], qcB[QC ? KS : 1][4];
   auto load_qc = [&](int rt, int ks, float* fa, float* fb)
       __attribute__((always_inline)) {
@@ -930,6 +950,111 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     }
   };
 
+  // 1/2-bit codes (key groups of one or a few tiles) cut the per-group
+  // work.  Both start from fixed fp16 hi + lo pairs of q * c0 * 2^KW over
+  // the key-group channel pairs, built once when the run leaves the ring,
+  // and take a group's start sum_c q c0 z as an MFMA of its zero-point
+  // pairs (the same for all 16 tokens) against those pairs, times 2^-KW.
+  //   1-bit (KW = 1): the key scales go into the decoded codes
+  //     (declow_ks: code s / 2 is exact), so those pairs are Q' itself and
+  //     a group only brings its scale pairs.
+  //   2-bit (KW = 0): code s is not always an fp16 value, so Q' = q c0 s is
+  //     rebuilt per group with packed fp16 operations from the fixed pairs:
+  //     hi' = RN(qh s), lo' = RN(RN(qh s - hi') + ql s), where qh s - hi'
+  //     is exact (the residual of a product of two 11-bit significands
+  //     under its rounding fits 11 bits), so hi' + lo' carries ~22 bits.
+  constexpr bool KSC = C::LOW && C::W == 1;           // scales in the codes
+  constexpr int KW = KSC ? 1 : 0;
+  constexpr bool QH = C::LOW && !KSC && NRT == 1;     // fixed pairs kept
+  constexpr unsigned LMASK = ((1u << C::W) - 1u) * (0x00010001u << (10 - C::W));
+  const unsigned l_one = KSC ? vreg(0x3C003C00u) : 0u;            // fp16 (1, 1)
+  const unsigned l_mask = KSC ? __builtin_amdgcn_readfirstlane(vreg(LMASK)) : 0u;
+  unsigned ksp[KSC ? KS : 1][4];       // key scale pairs of the current group
+  u4v qch[QH ? KS : 1], qcl[QH ? KS : 1];
+  // hi + lo pairs of q * c0 * 2^KW of row tile rt over k-step ks's pairs
+  auto qc_pairs = [&](int rt, int ks, u4v& h4, u4v& l4) __attribute__((always_inline)) {
+    float fa[4], fb[4];
+    load_qc(rt, ks, fa, fb);
+    unsigned hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float xa = opaque(fa[j] * (float)(1 << KW));
+      const float xb = opaque(fb[j] * (float)(1 << KW));
+      hi[j] = pack2(xa, xb);
+      lo[j] = pack2(xa - h_lo(hi[j]), xb - h_hi(hi[j]));
+    }
+    h4 = u4v{hi[0], hi[1], hi[2], hi[3]};
+    l4 = u4v{lo[0], lo[1], lo[2], lo[3]};
+  };
+  auto build_lowq = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (KSC) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) qc_pairs(rt, ks, bqh[rt][ks], bql[rt][ks]);
+      } else if constexpr (QH) {
+        qc_pairs(0, ks, qch[ks], qcl[ks]);
+      }
+    }
+  };
+  auto build_lowk = [&](const unsigned char* ksz) __attribute__((always_inline)) {
+    f4v cc[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) cc[rt] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cA = chan_a(ks);
+      const u4v sA = *(const u4v*)(ksz + 4 * cA);          // {s, z} of cA .. cA+3
+      const u4v sB = *(const u4v*)(ksz + 4 * (cA + DAB));
+      unsigned sp[4], zp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sp[j] = __builtin_amdgcn_perm(sB[j], sA[j], 0x05040100u);
+        zp[j] = __builtin_amdgcn_perm(sB[j], sA[j], 0x07060302u);
+      }
+      const u4v az = u4v{zp[0], zp[1], zp[2], zp[3]};
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        if constexpr (KSC) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ksp[ks][j] = sp[j];
+          cc[rt] = mfma16(az, bqh[rt][ks], cc[rt]);
+          cc[rt] = mfma16(az, bql[rt][ks], cc[rt]);
+        } else {
+          u4v h4, l4;
+          if constexpr (QH) {
+            h4 = qch[ks];
+            l4 = qcl[ks];
+          } else {
+            qc_pairs(rt, ks, h4, l4);
+          }
+          cc[rt] = mfma16(az, h4, cc[rt]);
+          cc[rt] = mfma16(az, l4, cc[rt]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+#pragma clang fp contract(off)        // hi must stay the rounded product
+            // (vector elements go through scalars: a bit cast of h4[j]
+            // itself reads element 0 whatever j is)
+            const unsigned hw = h4[j], lw = l4[j], sw = sp[j];
+            const h2v qh = __builtin_bit_cast(h2v, hw);
+            const h2v ql = __builtin_bit_cast(h2v, lw);
+            const h2v sv = __builtin_bit_cast(h2v, sw);
+            const h2v hi = qh * sv;
+            const h2v lo = __builtin_elementwise_fma(
+                ql, sv, __builtin_elementwise_fma(qh, sv, -hi));
+            bqh[rt][ks][j] = __builtin_bit_cast(unsigned, hi);
+            bql[rt][ks][j] = __builtin_bit_cast(unsigned, lo);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      binit[rt] = cc[rt][0] * (1.f / (float)(1 << KW));
+      refresh(rt);
+    }
+  };
+
   // S^T = K Q'^T for the two 16-token subtiles, started at cinit.
   auto scores = [&](f4v (&sc)[2][NRT], const u4v (&ak)[2][KS])
       __attribute__((always_inline)) {
@@ -990,6 +1115,14 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   // ---- one quantized 32-token tile from LDS
   auto quant_tile = [&](const unsigned char* tb, int t, int j, bool may_build, int u, bool next)
       __attribute__((always_inline)) {
+    if constexpr (C::LOW) {    // the decode below needs the group's scales
+      const int grp = group_of(t);
+      if (may_build && grp != cur_grp) {
+        if (cur_grp < 0) build_lowq();
+        build_lowk(tb + C::O_KSZ);
+        cur_grp = grp;
+      }
+    }
     u4v ak[2][KS];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -1017,8 +1150,13 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
         } else {
           constexpr int KPD = 16 / C::W / 4;   // k-steps per dword
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            r[j] = declow<C::W>(kh[ks / KPD], 4 * (ks % KPD) + j, dk);
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (KSC)
+              r[j] = declow_ks<C::W>(kh[ks / KPD], 4 * (ks % KPD) + j, ksp[ks][j],
+                                     l_one, l_mask);
+            else
+              r[j] = declow<C::W>(kh[ks / KPD], 4 * (ks % KPD) + j, dk);
+          }
         }
         ak[st][ks] = u4v{r[0], r[1], r[2], r[3]};
       }
@@ -1026,10 +1164,12 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     if constexpr (DIRECTK) {   // key and scale registers are free now
       if (next) fetch_quant(__builtin_amdgcn_readfirstlane(u + 1), 1);
     }
-    const int grp = group_of(t);
-    if (may_build && grp != cur_grp) {
-      build_quant(tb + C::O_KSZ);
-      cur_grp = grp;
+    if constexpr (!C::LOW) {
+      const int grp = group_of(t);
+      if (may_build && grp != cur_grp) {
+        build_quant(tb + C::O_KSZ);
+        cur_grp = grp;
+      }
     }
     f4v sc[2][NRT];
     scores(sc, ak);
