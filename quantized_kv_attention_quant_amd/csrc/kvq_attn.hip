@@ -31,8 +31,10 @@
 //     Q' = q * s * sm_scale * log2(e) once per key group, kept as two fp16
 //     parts (hi + lo, two MFMAs) so the scores carry ~22 bits of Q'; the 1024
 //     offset (an MFMA of a constant operand with Q') and the zero-points go
-//     into the accumulator's initial value.  1/2-bit caches (groups of 32
-//     tokens) cut that per-group work: 1-bit codes carry their key scales
+//     into the accumulator's initial value.  1/2-bit codes decode as
+//     1 + code 2^-W instead (no subtract; the offset 1 leaves the fp32 sums
+//     with no cancellation to speak of), and their caches (groups of 32
+//     tokens) cut the per-group work: 1-bit codes carry their key scales
 //     themselves (code s / 2 is exact), 2-bit groups rebuild Q' with packed
 //     fp16 operations from fixed hi + lo parts of q * c0, and both take the
 //     zero-point term as one MFMA.  Per-token value scales are
@@ -229,24 +231,25 @@ __device__ __forceinline__ void dec4(unsigned H, unsigned* r, const DecK& k) {
   r[3] = ((H >> 8) & k.m_f0) | k.magic;
 }
 
-// W-bit codes: the pair at bits (W*i, 16 + W*i) as exact fp16 codes.
+// W-bit codes under the fp16 exponent of 1.0: the pair at bits (W*i,
+// 16 + W*i) becomes the top mantissa bits, x = 1 + code 2^-W (exact; the
+// offset 1 is at most a few codes, so taking it out of an fp32 sum later
+// costs no precision, unlike the 1024 of the 0x6400 form).  `one` is the
+// fp16 pair (1, 1), `m` the code bits' mask at their place under it.
 template <int W>
-__device__ __forceinline__ unsigned declow(unsigned H, int i, const DecK& k) {
-  constexpr unsigned mask = ((1u << W) - 1u) * 0x00010001u;
-  return hadd2(((H >> (W * i)) & mask) | k.magic, kMinus1024);
+__device__ __forceinline__ unsigned lowx(unsigned H, int i, unsigned one,
+                                         unsigned m) {
+  const int sh = (10 - W) - W * i;   // a constant once the caller unrolls
+  const unsigned x = sh >= 0 ? H << (sh & 31) : H >> (-sh & 31);
+  return (x & m) | one;
 }
 
-// W-bit key codes times their channels' key scales: the pair at bits
-// (W*i, 16 + W*i) goes under the fp16 exponent of 1.0 as the top mantissa
-// bits, x = 1 + code 2^-W (exact), and fma(x, s, -s) = code s 2^-W with a
-// single rounding (x s < 2 s: no overflow).  `one` is the fp16 pair
-// (1, 1), `m` the code bits' mask at their place under it.
+// ... times their channels' key scales: fma(x, s, -s) = code s 2^-W with a
+// single rounding (x s < 2 s: no overflow), exact for 1-bit codes.
 template <int W>
 __device__ __forceinline__ unsigned declow_ks(unsigned H, int i, unsigned s,
                                               unsigned one, unsigned m) {
-  const int sh = (10 - W) - W * i;   // a constant once the caller unrolls
-  const unsigned x = sh >= 0 ? H << (sh & 31) : H >> (-sh & 31);
-  const h2v xv = __builtin_bit_cast(h2v, (x & m) | one);
+  const h2v xv = __builtin_bit_cast(h2v, lowx<W>(H, i, one, m));
   const h2v sv = __builtin_bit_cast(h2v, s);
   return __builtin_bit_cast(unsigned, __builtin_elementwise_fma(xv, sv, -sv));
 }
@@ -293,7 +296,12 @@ struct Cfg {
   static constexpr int MT = D / 16;              // 16-channel output tiles
   static constexpr float KBIAS =
       PATH == P_T8 ? 1024.f : PATH == P_D4 ? 1016.5f : 0.f;
-  static constexpr unsigned NEG = PATH == P_D4 ? kMinusDraft : kMinus1024;
+  // code offset of the value decode: 1024 for the 0x6400 form, and for
+  // 1/2-bit codes (decoded as 1 + code 2^-W, accumulated times 2^W) 2^W
+  static constexpr unsigned NEG = PATH == P_D4   ? kMinusDraft
+                                  : PATH == P_L2 ? 0xC400C400u    // (-4, -4)
+                                  : PATH == P_L1 ? 0xC000C000u    // (-2, -2)
+                                                 : kMinus1024;
   // stage layout of one quantized tile (bytes)
   static constexpr int PL = 4 * D * W;           // one code plane
   static constexpr int VSZB = 128 * NG;          // value scale/zero pairs
@@ -951,24 +959,28 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
   };
 
   // 1/2-bit codes (key groups of one or a few tiles) cut the per-group
-  // work.  Both start from fixed fp16 hi + lo pairs of q * c0 * 2^KW over
-  // the key-group channel pairs, built once when the run leaves the ring,
-  // and take a group's start sum_c q c0 z as an MFMA of its zero-point
-  // pairs (the same for all 16 tokens) against those pairs, times 2^-KW.
-  //   1-bit (KW = 1): the key scales go into the decoded codes
-  //     (declow_ks: code s / 2 is exact), so those pairs are Q' itself and
-  //     a group only brings its scale pairs.
-  //   2-bit (KW = 0): code s is not always an fp16 value, so Q' = q c0 s is
+  // work.  Both decode codes as x = 1 + code 2^-W (lowx), start from fixed
+  // fp16 hi + lo pairs of q * c0 * 2^W over the key-group channel pairs,
+  // built once when the run leaves the ring, and take a group's start
+  // sum_c q c0 z as an MFMA of its zero-point pairs (the same for all 16
+  // tokens) against those pairs, times 2^-W.
+  //   1-bit: the key scales go into the decoded codes (declow_ks: code s / 2
+  //     is exact), so those pairs are Q' itself and a group only brings its
+  //     scale pairs.
+  //   2-bit: code s is not always an fp16 value, so Q4 = 4 q c0 s is
   //     rebuilt per group with packed fp16 operations from the fixed pairs:
   //     hi' = RN(qh s), lo' = RN(RN(qh s - hi') + ql s), where qh s - hi'
   //     is exact (the residual of a product of two 11-bit significands
   //     under its rounding fits 11 bits), so hi' + lo' carries ~22 bits.
+  //     Q4 x = Q4 + Q' code, so the start also takes - sum_c 4 q c0 s, an
+  //     MFMA of the scale pairs against the fixed pairs (it differs from
+  //     the sum of the rebuilt parts by their own ~2^-22 rounding).
   constexpr bool KSC = C::LOW && C::W == 1;           // scales in the codes
-  constexpr int KW = KSC ? 1 : 0;
+  constexpr int KW = C::LOW ? C::W : 0;
   constexpr bool QH = C::LOW && !KSC && NRT == 1;     // fixed pairs kept
   constexpr unsigned LMASK = ((1u << C::W) - 1u) * (0x00010001u << (10 - C::W));
-  const unsigned l_one = KSC ? vreg(0x3C003C00u) : 0u;            // fp16 (1, 1)
-  const unsigned l_mask = KSC ? __builtin_amdgcn_readfirstlane(vreg(LMASK)) : 0u;
+  const unsigned l_one = C::LOW ? vreg(0x3C003C00u) : 0u;         // fp16 (1, 1)
+  const unsigned l_mask = C::LOW ? __builtin_amdgcn_readfirstlane(vreg(LMASK)) : 0u;
   unsigned ksp[KSC ? KS : 1][4];       // key scale pairs of the current group
   u4v qch[QH ? KS : 1], qcl[QH ? KS : 1];
   // hi + lo pairs of q * c0 * 2^KW of row tile rt over k-step ks's pairs
@@ -998,9 +1010,9 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     }
   };
   auto build_lowk = [&](const unsigned char* ksz) __attribute__((always_inline)) {
-    f4v cc[NRT];
+    f4v cc[NRT], co[NRT];
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) cc[rt] = f4v{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < NRT; ++rt) cc[rt] = co[rt] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int cA = chan_a(ks);
@@ -1030,6 +1042,9 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
           }
           cc[rt] = mfma16(az, h4, cc[rt]);
           cc[rt] = mfma16(az, l4, cc[rt]);
+          const u4v as = u4v{sp[0], sp[1], sp[2], sp[3]};
+          co[rt] = mfma16(as, h4, co[rt]);
+          co[rt] = mfma16(as, l4, co[rt]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
 #pragma clang fp contract(off)        // hi must stay the rounded product
@@ -1050,7 +1065,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     }
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      binit[rt] = cc[rt][0] * (1.f / (float)(1 << KW));
+      binit[rt] = cc[rt][0] * (1.f / (float)(1 << KW)) - co[rt][0];
       refresh(rt);
     }
   };
@@ -1155,7 +1170,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
               r[j] = declow_ks<C::W>(kh[ks / KPD], 4 * (ks % KPD) + j, ksp[ks][j],
                                      l_one, l_mask);
             else
-              r[j] = declow<C::W>(kh[ks / KPD], 4 * (ks % KPD) + j, dk);
+              r[j] = lowx<C::W>(kh[ks / KPD], 4 * (ks % KPD) + j, l_one, l_mask);
           }
         }
         ak[st][ks] = u4v{r[0], r[1], r[2], r[3]};
@@ -1209,7 +1224,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
           const unsigned q = hmul2(pp[i], sz[i * NG + gg]);
           bp[rt][gg][i] = q;
           z = dot2(pp[i], sz[4 * NG + i * NG + gg], z);
-          if constexpr (!C::LOW) z = dot2(q, C::NEG, z);   // code offset
+          z = dot2(q, C::NEG, z);                           // code offset
         }
         zacc[rt][gg] = z;
       }
@@ -1249,7 +1264,7 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
         constexpr int PER = 4 / C::W;   // channel tiles per dword
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          r[j] = declow<C::W>(vh[mt / PER], 4 * (mt % PER) + j, dk);
+          r[j] = lowx<C::W>(vh[mt / PER], 4 * (mt % PER) + j, l_one, l_mask);
       }
       const u4v av = u4v{r[0], r[1], r[2], r[3]};
 #pragma unroll
@@ -1299,7 +1314,9 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
         }
       softmax(rt, sc[0][rt], sc[1][rt]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bpres[rt][i] = pack2(sc[0][rt][i], sc[1][rt][i]);
+      for (int i = 0; i < 4; ++i)   // (times 2^-W: 1/2-bit sums are scaled by 2^W)
+        bpres[rt][i] = pack2(sc[0][rt][i] * (1.f / (float)(1 << KW)),
+                             sc[1][rt][i] * (1.f / (float)(1 << KW)));
     }
   };
 
@@ -1401,7 +1418,8 @@ __global__ void __launch_bounds__((Cfg<PATH, D, NG, NRT, PAIR>::NW * 64))
     for (int gg = 0; gg < NG; ++gg) zacc[rt][gg] = sum_x4(zacc[rt][gg]) * kOScale;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      acc[rt][mt] = acc[rt][mt] * kOScale + zacc[rt][mt / (MT / NG)];
+      acc[rt][mt] = acc[rt][mt] * (kOScale * (float)(1 << KW)) +
+                    zacc[rt][mt / (MT / NG)];
   }
 
   // ---- merge the NS streams through LDS in one step: every stream writes
