@@ -192,7 +192,11 @@ size_t kv_attn_workspace_bytes(const kvq_cache* c, int T, int Hq);
  *   launches (split pass, then log-sum-exp merge).  Calls sharing one ws
  *   must be ordered (same stream).
  *   Range: value groups need scale s <= 63 (the PV step multiplies fp16
- *   probabilities scaled to at most 2^10 by s in fp16); every input finite.
+ *   probabilities scaled to at most 2^10 by s in fp16); per channel, the
+ *   query times sm_scale * log2(e) times the key scale s of the channel's
+ *   group must stay below 65504 in magnitude (below 16376 for 2-bit
+ *   caches: the product is kept as fp16 parts, for 2-bit codes times 4);
+ *   every input finite.
  *   Rows: one launch pair handles the T * Hq/Hkv query rows of a kv head
  *   up to 32; above that, the query heads of each kv group run in
  *   consecutive launch pairs of 32 / T heads (each reading the cache).

@@ -97,11 +97,14 @@ def lse_tolerance(rep, q16, path, sm_scale):
     arithmetic.  Scores use Q' = q*s*c0 (quantized keys) or q*c0 (fp16 keys)
     split into two fp16 parts, so each channel term carries a relative error
     of at most 2^-21; the MFMA accumulates terms Q' * a in fp32 (a = 1024 +
-    code <= 1279 for 8-bit codes, a = code for 1/2-bit), whose partial sums
-    stay below max(a) * sum_c |Q'_c| and take ~16 roundings of 2^-24.  Every
-    logit, and so the log-sum-exp, moves by at most
-    2^-21 sm sum_c|q_c k^_jc| + 16 2^-24 max(a) sm sum_c |q_c| s_gc;
-    the bound doubles that and adds 2e-6 for exp2/log2 and the merge."""
+    code <= 1279 for 8-bit codes, a = code for 1-bit, and for 2-bit codes
+    a = 4 (1 + code/4) <= 7 against 4 Q', with 4 sum_c q c0 s taken out of
+    the start), whose partial sums stay below max(a) * sum_c |Q'_c| and take
+    ~16 roundings of 2^-24.  Every logit, and so the log-sum-exp, moves by
+    at most 2^-21 sm sum_c|q_c k^_jc| + e sm sum_c |q_c| s_gc, with
+    e = 16 2^-24 max(a), plus 4 2^-21 for 2-bit codes (their start takes
+    the exact q c0 s, not its two rounded fp16 parts); the bound doubles
+    that and adds 2e-6 for exp2/log2 and the merge."""
     from oracle import attention as oatt
     B, T, Hq, d = q16.shape
     gs = Hq // rep.Hkv
@@ -115,12 +118,13 @@ def lse_tolerance(rep, q16, path, sm_scale):
             qa = np.abs(q16[b, :, h * gs:(h + 1) * gs].astype(np.float64))
             mag = np.einsum("thc,jc->thj", qa, np.abs(K)).max(axis=2)
             s = rep.ks[b, h].astype(np.float64)
-            # largest MFMA operand: 1024 + code for 8-bit codes, the code
-            # itself (< 2^bits) for 1/2-bit codes
-            top = 1279.0 if rep.bits == 8 else float((1 << rep.bits) - 1)
+            # largest MFMA operand against Q': 1024 + code for 8-bit codes,
+            # the code for 1-bit, 4 (1 + 3/4) for 2-bit
+            top = {8: 1279.0, 2: 7.0, 1: 1.0}[rep.bits]
+            e = 16 * 2.0 ** -24 * top + (4 * 2.0 ** -21 if rep.bits == 2 else 0.0)
             acc = (np.einsum("thc,gc->thg", qa, s).max(axis=2) if s.size
                    else np.zeros_like(mag))
-            bound = sm_scale * (2.0 ** -21 * mag + 16 * 2.0 ** -24 * top * acc)
+            bound = sm_scale * (2.0 ** -21 * mag + e * acc)
             tol[b, h * gs:(h + 1) * gs] = (2 * bound).T
     return tol + 2e-6
 

@@ -7,7 +7,8 @@
   a batch of blocks (few splits);
 * GQA equal to MHA with the kv heads repeated;
 * value scales at the attention kernels' limit (s = 63, where the fp16
-  product of a probability scaled to 2^10 and s is largest).
+  product of a probability scaled to 2^10 and s is largest);
+* key scales times queries near the range the key operands hold in fp16.
 """
 import numpy as np
 import pytest
@@ -191,6 +192,46 @@ def test_value_scale_at_the_limit(bits):
     torch.cuda.synchronize()
     ref, _ = attention.attend(rep, q16, "target", w.d ** -0.5)
     assert_attn_close(out.cpu().numpy(), ref, f"value scale 63, {bits}-bit")
+
+
+@pytest.mark.parametrize("bits", [8, 2, 1])
+def test_lowbit_key_range(bits):
+    """One key group with a large scale and a large query component on its
+    channel: q c0 s at 90% of what a 2-bit cache's key operands hold in
+    fp16 (4 q c0 s < 65504, c0 = sm_scale log2 e), one token's logit ahead
+    of every other by thousands.  Outputs finite and within the bar (the
+    row's attention is that token's value), for every code width."""
+    G = 128 if bits == 8 else 32
+    Gv = 64 if bits == 8 else 32
+    w = W(f"krange_{bits}", 1, 8, 2, 128, 900, G, Gv, 256 if bits == 8 else 32,
+          bits, "normal")
+    say(f"[gpu] key scale x query near the fp16 range, {bits}-bit")
+    K, V = host_tokens(w, 6)
+    A = np.float16(1500.0)
+    g0 = 2 * G                                   # a quantized group
+    K[0, g0:g0 + G, :, 0] = 0
+    K[0, g0 + 5, :, 0] = A                       # the dominant token
+    K[0, g0 + 9, :, 0] = -A
+    cache = kq.QuantKVCache(shape_for(w))
+    cache.append(to_dev(K), to_dev(V))
+    rep = ocache.Replay(1, w.Hkv, w.d, w.G, w.Gv, w.bits, w.R)
+    rep.append(K, V)
+    assert g0 + G <= rep.n_q
+    s = float(rep.ks[0, 0, g0 // G, 0])
+    sm = w.d ** -0.5
+    c0 = sm * np.log2(np.e)
+    qv = 0.9 * 65504 / (4 * c0 * s)
+    assert 10 < qv < 60000
+    q16 = synth.queries(w, 3, 2)
+    q16[..., 0] = np.float16(qv)
+    out, lse = cache.verify(to_dev(q16), want_lse=True)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all() and np.isfinite(lse.cpu().numpy()).all()
+    ref, ref_lse = attention.attend(rep, q16, "target", sm)
+    assert_attn_close(got, ref, f"key range, {bits}-bit")
+    tol = lse_tolerance(rep, q16, "target", sm)
+    assert (np.abs(lse.cpu().numpy() - ref_lse) <= tol).all()
 
 
 @pytest.mark.parametrize("bits", [8, 2])
