@@ -51,6 +51,9 @@ SMALL = {
     # group sizes that are not powers of two (top-k pads them to 4 and 8)
     "gqa3_2bit": W("gqa3_2bit", 1, 6, 2, 128, 2000, 32, 32, 32, 2, "normal"),
     "gqa7": W("gqa7", 1, 14, 2, 128, 1500, 64, 64, 128, 8, "outlier"),
+    # 1/2-bit caches with 8 query heads per kv head: head subsets
+    "gqa8_2bit": W("gqa8_2bit", 1, 16, 2, 128, 1500, 32, 32, 32, 2, "normal"),
+    "gqa8_1bit": W("gqa8_1bit", 1, 16, 2, 128, 1500, 32, 32, 32, 1, "normal"),
 }
 
 
@@ -136,7 +139,11 @@ RUNS = [("tiny", "target", 1), ("tiny", "draft4", 1), ("tiny", "target", 8),
         ("d64_g256_2bit", "target", 3),
         # 40 rows (heads 0-5, then 6-7), 64 rows (2 x 4 heads), 128 rows
         ("gqa8", "target", 5), ("gqa8", "target", 8), ("gqa8", "draft4", 16),
-        ("gqa3_2bit", "target", 2), ("gqa7", "target", 4)]
+        ("gqa3_2bit", "target", 2), ("gqa7", "target", 4),
+        # 1-bit codes in two-wave streams (32 rows); 1/2-bit codes over head
+        # subsets: 40 rows (6 + 2 heads), 48 rows (5 + 3 heads)
+        ("gqa_1bit", "target", 8), ("gqa8_2bit", "target", 5),
+        ("gqa8_1bit", "target", 6)]
 
 
 @pytest.mark.parametrize("name,path,T", RUNS)
