@@ -36,6 +36,12 @@ CASES = [
      "target", 6, 4),
     ("mha_d64_t16_draft", W("mha_d64_int8", 1, 3, 3, 64, 777, 64, 32, 128, 8,
                             "outlier"), "draft4", 16, 7),
+    # 1-bit codes in two-wave streams (32 rows), and a 2-bit cache with 8
+    # query heads per kv head at T = 5 (40 rows: head subsets of 6 and 2)
+    ("gqa_1bit_t8", W("gqa_1bit", 2, 8, 2, 128, 1000, 32, 32, 32, 1, "normal"),
+     "target", 8, 5),
+    ("gqa8_2bit_t5", W("gqa8_2bit", 1, 16, 2, 128, 1500, 32, 32, 32, 2,
+                       "normal"), "target", 5, 2),
 ]
 
 

@@ -219,7 +219,8 @@ def test_verify_row_equals_prefix_decode():
     ("g32_bulk", "target", 128), ("long_2bit", "target", 256),
     ("g256", "target", 64), ("d64_g256_2bit", "target", 32),
     ("gqa3_2bit", "target", 64), ("gqa7", "target", 100),
-    ("gqa7", "draft4", 64)])
+    ("gqa7", "draft4", 64), ("gqa8_2bit", "target", 64),
+    ("gqa8_1bit", "target", 32)])
 def test_topk_bit_exact(name, path, k):
     w = SMALL[name]
     say(f"[gpu] topk {name} {path} k={k}")
