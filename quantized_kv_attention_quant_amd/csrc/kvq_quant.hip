@@ -452,13 +452,14 @@ __device__ __forceinline__ void ring_token(const AppendArgs& a, int item, int b,
 
 // One kernel per (head dim, code width, key groups per item): a launch runs
 // only its own item code (a single kernel holding every instantiation
-// measured slower on the low-bit fills).  The 8-bit kernels are held to 96
-// VGPRs for five waves per SIMD (117 and four waves unconstrained): the
-// ~24 registers spilled cost less than the fifth wave gains (32K prefill
-// 54.0 against 56.1 us); the low-bit kernels (107-108 VGPRs) keep four.
+// measured slower on the low-bit fills).  The 8-bit and 1-bit kernels are
+// held to 96 VGPRs for five waves per SIMD (117 and 107 unconstrained, four
+// waves): the registers spilled cost less than the fifth wave gains (32K
+// prefill 54.0 against 56.1 us, batched 1-bit fill 1.33 against 1.40 ms);
+// the 2-bit kernels (108) keep four, where five measured 1-2% slower.
 template <int D, int W, int NGI>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(W == 4 ? 5 : 4)))
+__attribute__((amdgpu_waves_per_eu(W == 2 ? 4 : 5)))
 append_kernel(AppendArgs a, Item it) {
   __shared__ unsigned lds_hi[128 * 4];
   __shared__ unsigned lds_lo[128 * 4];
